@@ -1,0 +1,266 @@
+"""Checks that tie the oracle to facts fixed outside it.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+(or the oracle's own error) if the oracle disagrees with:
+
+- a library routine: torch's scaled_dot_product_attention in float64, with its
+  own grouped-query mapping and its own lower-right causal mask, on K/V kept
+  contiguous in token order (the unpaged definition);
+- an invariance the indirection must have: relabelling physical blocks changes
+  nothing;
+- closed forms: one key returns its value row; a zero query or identical keys
+  return the plain mean of the value rows;
+- cross-path identities: prefill of one token equals decode; a prefill split
+  into chunks equals the unsplit one; sequences sharing prefix blocks and new
+  rows give the same outputs.
+
+They are written so that the planted mistakes the oracle can be built with
+(dropped key, wrong head grouping, missing scale, off-by-one page index, K read
+as V) each fail at least one of them; ``test_oracle_plants.py`` checks that.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence, Tuple
+
+import torch
+import torch.nn.functional as F
+from torch.nn.attention.bias import causal_lower_right
+
+import oracle as O
+from workloads import SeqState, custom_plan, make_tensors
+
+TOL = 1e-12  # float64 oracle against float64 library results
+
+
+def _store_all(orc, plan, tens):
+    """Store every new row of ``plan`` with the oracle; returns its metadata."""
+    meta = O.prepare_prefill(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    orc.store(tens.k_cache(), tens.v_cache(), tens.k_new(), tens.v_new(), meta["slot_mapping"])
+    return meta
+
+
+def _contiguous_kv(plan, tens, b):
+    """K/V rows of sequence b in token order, straight from the new-row tensors
+    (every token of the sequence is new in the plans built here)."""
+    starts = [0]
+    for s in plan.seqs:
+        starts.append(starts[-1] + s.num_new)
+    k = tens.k_new()[starts[b]:starts[b + 1]].double()
+    v = tens.v_new()[starts[b]:starts[b + 1]].double()
+    return k, v  # [L, H_kv, d]
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """q [nq, H_q, d], k/v [nk, H_kv, d] -> [nq, H_q, d] float64 via torch."""
+    o = F.scaled_dot_product_attention(
+        q.double().transpose(0, 1).unsqueeze(0),
+        k.transpose(0, 1).unsqueeze(0),
+        v.transpose(0, 1).unsqueeze(0),
+        attn_mask=mask, scale=scale, enable_gqa=True,
+    )
+    return o.squeeze(0).transpose(0, 1)
+
+
+def _full_plan(lens, bs, H_q, H_kv, d, seed, extra=3):
+    return custom_plan([(0, n) for n in lens], bs, H_q, H_kv, d, seed=seed,
+                       extra_blocks=extra, kind="prefill")
+
+
+GEOMS = [  # (block_size, H_q, H_kv, d)
+    (16, 4, 2, 64),
+    (16, 8, 2, 64),
+    (32, 4, 4, 64),
+    (16, 8, 1, 128),
+]
+
+
+def pin_decode_equals_library(orc):
+    for gi, (bs, H_q, H_kv, d) in enumerate(GEOMS):
+        lens = [1, 5, bs, bs + 1, 3 * bs - 2]
+        plan = _full_plan(lens, bs, H_q, H_kv, d, seed=10 + gi)
+        tens = make_tensors(plan, "cpu", poison=True)
+        _store_all(orc, plan, tens)
+        dec = [SeqState(s.block_ids, s.total - 1, 1) for s in plan.seqs]
+        meta = O.prepare_decode(dec, bs, plan.max_blocks_per_seq)
+        g = torch.Generator().manual_seed(99 + gi)
+        q = torch.randn(len(lens), H_q, d, generator=g).to(torch.bfloat16)
+        scale = 1.0 / math.sqrt(d)
+        out = orc.decode(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                         meta["context_lens"], scale)
+        assert torch.isfinite(out).all()
+        for b in range(len(lens)):
+            k, v = _contiguous_kv(plan, tens, b)
+            ref = _sdpa(q[b:b + 1], k, v, float(torch.tensor(scale, dtype=torch.float32)))
+            err = (out[b] - ref[0]).abs().max().item()
+            assert err < TOL, f"decode vs library: seq {b} geom {gi} err {err}"
+
+
+def pin_prefill_equals_library(orc):
+    """Causal prefill over a cached prefix, bottom-right aligned, vs torch."""
+    for gi, (bs, H_q, H_kv, d) in enumerate(GEOMS):
+        specs = [(0, 7), (bs, 5), (2 * bs + 3, bs + 2), (5, 1), (0, 2 * bs + 1)]
+        plan = _full_plan([c + n for c, n in specs], bs, H_q, H_kv, d, seed=20 + gi)
+        tens = make_tensors(plan, "cpu", poison=True)
+        _store_all(orc, plan, tens)
+        view = [SeqState(s.block_ids, c, n) for s, (c, n) in zip(plan.seqs, specs)]
+        meta = O.prepare_prefill(view, bs, plan.max_blocks_per_seq)
+        g = torch.Generator().manual_seed(7 + gi)
+        T = sum(n for _, n in specs)
+        q = torch.randn(T, H_q, d, generator=g).to(torch.bfloat16)
+        scale = 1.0 / math.sqrt(d)
+        out = orc.prefill(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                          meta["cu_seqlens_q"], meta["cu_seqlens_k"], scale)
+        assert torch.isfinite(out).all()
+        at = 0
+        for b, (c, n) in enumerate(specs):
+            k, v = _contiguous_kv(plan, tens, b)
+            mask = causal_lower_right(n, c + n)
+            ref = _sdpa(q[at:at + n], k, v, float(torch.tensor(scale, dtype=torch.float32)), mask)
+            err = (out[at:at + n] - ref).abs().max().item()
+            assert err < TOL, f"prefill vs library: seq {b} geom {gi} err {err}"
+            at += n
+
+
+def _relabel(plan, tens, perm):
+    """Same logical content under physical ids perm[p]."""
+    pool = torch.empty_like(tens.pool)
+    pool[:, :, perm] = tens.pool
+    seqs = [SeqState(tuple(int(perm[p]) for p in s.block_ids), s.num_cached, s.num_new)
+            for s in plan.seqs]
+    return pool, seqs
+
+
+def pin_permutation_invariance(orc):
+    bs, H_q, H_kv, d = 16, 8, 2, 64
+    specs = [(0, 3), (40, 9), (16, 16), (70, 1)]
+    plan = custom_plan(specs, bs, H_q, H_kv, d, seed=5, extra_blocks=4, kind="prefill")
+    tens = make_tensors(plan, "cpu", poison=True)
+    meta = _store_all(orc, plan, tens)
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(plan.total_new, H_q, d, generator=g).to(torch.bfloat16)
+    out = orc.prefill(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                      meta["cu_seqlens_q"], meta["cu_seqlens_k"], 0.125)
+    perm = torch.randperm(plan.num_blocks, generator=g)
+    pool2, seqs2 = _relabel(plan, tens, perm)
+    meta2 = O.prepare_prefill(seqs2, bs, plan.max_blocks_per_seq)
+    out2 = orc.prefill(q, pool2[0, 0], pool2[1, 0], meta2["block_tables"],
+                       meta2["cu_seqlens_q"], meta2["cu_seqlens_k"], 0.125)
+    assert torch.equal(out, out2), "relabelling physical blocks changed the output"
+    # the relabelled tables really differ
+    assert meta["block_tables"] != meta2["block_tables"]
+
+
+def pin_closed_forms(orc):
+    bs, H_q, H_kv, d = 16, 4, 2, 64
+    # (a) a sequence of one token returns that token's value row, exactly
+    plan = _full_plan([1, 1, 1], bs, H_q, H_kv, d, seed=31)
+    tens = make_tensors(plan, "cpu", poison=True)
+    _store_all(orc, plan, tens)
+    dec = [SeqState(s.block_ids, 0, 1) for s in plan.seqs]
+    meta = O.prepare_decode(dec, bs, plan.max_blocks_per_seq)
+    q = torch.randn(3, H_q, d).to(torch.bfloat16)
+    out = orc.decode(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                     meta["context_lens"], 0.125)
+    G = H_q // H_kv
+    for b in range(3):
+        for h in range(H_q):
+            assert torch.equal(out[b, h], tens.v_new()[b, h // G].double()), "one key != its value"
+    # (b) zero query: uniform weights -> plain mean of the value rows
+    # (c) identical keys: uniform weights as well
+    lens = [5, 33, 40]
+    for identical_keys in (False, True):
+        plan = _full_plan(lens, bs, H_q, H_kv, d, seed=32)
+        tens = make_tensors(plan, "cpu", poison=True)
+        if identical_keys:
+            at = 0
+            for n in lens:
+                tens.k_new()[at:at + n] = tens.k_new()[at:at + 1].clone()
+                at += n
+        _store_all(orc, plan, tens)
+        dec = [SeqState(s.block_ids, s.total - 1, 1) for s in plan.seqs]
+        meta = O.prepare_decode(dec, bs, plan.max_blocks_per_seq)
+        if identical_keys:
+            q = torch.randn(3, H_q, d).to(torch.bfloat16)
+        else:
+            q = torch.zeros(3, H_q, d, dtype=torch.bfloat16)
+        out = orc.decode(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                         meta["context_lens"], 0.125)
+        for b in range(3):
+            _, v = _contiguous_kv(plan, tens, b)
+            mean = v.mean(dim=0)  # [H_kv, d]
+            for h in range(H_q):
+                err = (out[b, h] - mean[h // G]).abs().max().item()
+                assert err < TOL, f"uniform-weight case: err {err}"
+
+
+def pin_prefill_one_equals_decode(orc):
+    bs, H_q, H_kv, d = 16, 8, 2, 64
+    lens = [1, 9, 16, 17, 50]
+    plan = custom_plan([(n - 1, 1) for n in lens], bs, H_q, H_kv, d, seed=41)
+    tens = make_tensors(plan, "cpu", poison=True)
+    mp = O.prepare_prefill(plan.seqs, bs, plan.max_blocks_per_seq)
+    md = O.prepare_decode(plan.seqs, bs, plan.max_blocks_per_seq)
+    orc.store(tens.k_cache(), tens.v_cache(), tens.k_new(), tens.v_new(), md["slot_mapping"])
+    q = tens.q[0]
+    a = orc.decode(q, tens.k_cache(), tens.v_cache(), md["block_tables"], md["context_lens"], 0.125)
+    b = orc.prefill(q, tens.k_cache(), tens.v_cache(), mp["block_tables"], mp["cu_seqlens_q"],
+                    mp["cu_seqlens_k"], 0.125)
+    assert torch.isfinite(a).all()
+    assert torch.equal(a, b), "prefill of one token != decode"
+
+
+def pin_chunked_prefill(orc):
+    bs, H_q, H_kv, d = 16, 4, 2, 64
+    specs = [(16, 30), (0, 21)]
+    plan = custom_plan(specs, bs, H_q, H_kv, d, seed=51, kind="prefill")
+    tens = make_tensors(plan, "cpu", poison=True)
+    meta = _store_all(orc, plan, tens)
+    q = tens.q[0]
+    full = orc.prefill(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                       meta["cu_seqlens_q"], meta["cu_seqlens_k"], 0.125)
+    # first chunk: n1 tokens; second chunk: the rest on top of a longer prefix
+    cut = [11, 8]
+    first = [SeqState(s.block_ids, c, n1) for s, (c, _), n1 in zip(plan.seqs, specs, cut)]
+    second = [SeqState(s.block_ids, c + n1, n - n1) for s, (c, n), n1 in zip(plan.seqs, specs, cut)]
+    m1 = O.prepare_prefill(first, bs, plan.max_blocks_per_seq)
+    m2 = O.prepare_prefill(second, bs, plan.max_blocks_per_seq)
+    rows1, rows2 = [], []
+    at = 0
+    for (c, n), n1 in zip(specs, cut):
+        rows1 += list(range(at, at + n1))
+        rows2 += list(range(at + n1, at + n))
+        at += n
+    o1 = orc.prefill(q[rows1], tens.k_cache(), tens.v_cache(), m1["block_tables"],
+                     m1["cu_seqlens_q"], m1["cu_seqlens_k"], 0.125)
+    o2 = orc.prefill(q[rows2], tens.k_cache(), tens.v_cache(), m2["block_tables"],
+                     m2["cu_seqlens_q"], m2["cu_seqlens_k"], 0.125)
+    assert torch.equal(full[rows1], o1) and torch.equal(full[rows2], o2), "chunking changed output"
+
+
+def pin_shared_prefix(orc):
+    bs, H_q, H_kv, d = 16, 4, 2, 64
+    specs = [(32, 5), (32, 5), (48, 3)]
+    plan = custom_plan(specs, bs, H_q, H_kv, d, seed=61, share_first=(2, 2), kind="prefill")
+    assert plan.seqs[0].block_ids[:2] == plan.seqs[1].block_ids[:2]
+    tens = make_tensors(plan, "cpu", poison=True)
+    tens.kv_new[0, 5:10] = tens.kv_new[0, 0:5]  # identical new rows for seqs 0 and 1
+    q = tens.q[0].clone()
+    q[5:10] = q[0:5]
+    meta = _store_all(orc, plan, tens)
+    out = orc.prefill(q, tens.k_cache(), tens.v_cache(), meta["block_tables"],
+                      meta["cu_seqlens_q"], meta["cu_seqlens_k"], 0.125)
+    assert torch.isfinite(out).all()
+    assert torch.equal(out[0:5], out[5:10]), "sequences sharing a prefix disagree"
+    assert not torch.equal(out[0:3], out[10:13])
+
+
+ATTENTION_PINS = [
+    pin_decode_equals_library,
+    pin_prefill_equals_library,
+    pin_permutation_invariance,
+    pin_closed_forms,
+    pin_prefill_one_equals_decode,
+    pin_chunked_prefill,
+    pin_shared_prefix,
+]
