@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of seeded synthetic input:
+the host metadata is prepared once (outside the timed region), then each step
+stores the new K/V rows (pkv_store) and runs attention (pkv_decode, or
+pkv_prefill_varlen for the prefill workload); the 28-layer workload does both
+for every layer.  Inputs are resident in HBM before timing starts.
+
+The JSON line reports the Qwen3-0.6B-shaped decode workload (B=256, H_q=16,
+H_kv=8, d=128, block size 256, context lengths U[128, 2048]) with its decode
+roofline (achieved algorithmic HBM bytes per decode call / the call's average
+duration, from HIP events on the launch stream) and the CPU oracle timed on a
+bounded sample.  The other workloads are reported under "secondary".
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: achieved HBM GB/s & % peak; prefill TFLOP/s; tokens/s"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+
+
+# ------------------------------------------------------------ workload arithmetic
+
+def decode_bytes(plan) -> int:
+    """Algorithmic bytes one decode call must move: K+V of every context token,
+    Q in and O out, context lengths, and the block-table entries read."""
+    kv = sum(2 * n * plan.H_kv * plan.d * 2 for n in plan.lens())
+    qo = 2 * plan.B * plan.H_q * plan.d * 2
+    tbl = 4 * sum(-(-n // plan.block_size) for n in plan.lens())
+    return kv + qo + 4 * plan.B + tbl
+
+
+def store_bytes(plan) -> int:
+    """K and V rows read and written, plus the slot of every row."""
+    n = plan.total_new
+    return 2 * n * plan.row_elems * 2 * 2 + 4 * n
+
+
+def prefill_flops(plan) -> int:
+    """Causal attention flops over unmasked (query, key) pairs: 4 d H_q per pair."""
+    pairs = sum(s.num_new * s.num_cached + s.num_new * (s.num_new + 1) // 2 for s in plan.seqs)
+    return 4 * plan.d * plan.H_q * pairs
+
+
+# ------------------------------------------------------------------- timing
+
+class Timer:
+    """HIP events recorded on the current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def span(self, name):
+        torch = self.torch
+        timer = self
+
+        class _Span:
+            def __enter__(self):
+                self.a = torch.cuda.Event(enable_timing=True)
+                self.b = torch.cuda.Event(enable_timing=True)
+                self.a.record()
+
+            def __exit__(self, *exc):
+                self.b.record()
+                timer.pairs.setdefault(name, []).append((self.a, self.b))
+
+        return _Span()
+
+    def mean_ms(self, name):
+        ev = self.pairs.get(name, [])
+        if not ev:
+            return float("nan")
+        return sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+
+def run_workload(name, steps, warmup, pools, torch, pkv, log):
+    from workloads import make_plan, make_tensors
+
+    plan = make_plan(name)
+    dev = "cuda"
+    t0 = time.time()
+    tens = [make_tensors(plan, dev, poison=False, seed=plan.seed + 17 * r) for r in range(pools)]
+    meta = pkv.prepare_metadata(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    dm = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in meta.items()}
+    scale = 1.0 / math.sqrt(plan.d)
+    ws = None
+    if plan.kind == "decode":
+        nbytes = pkv.decode_workspace_size(plan.B, plan.H_q, plan.H_kv, plan.d, plan.block_size,
+                                           plan.max_blocks_per_seq)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        outs = [torch.empty_like(t.q[0]) for t in tens]
+    torch.cuda.synchronize()
+    log(f"{name}: inputs ready in {time.time() - t0:.1f}s ({plan.B} seqs, {plan.num_blocks} blocks,"
+        f" {pools} pool(s))")
+
+    timer = Timer(torch)
+
+    def step(i, timed):
+        t = tens[i % pools]
+        for layer in range(plan.layers):
+            kc, vc = t.k_cache(layer), t.v_cache(layer)
+            if timed:
+                with timer.span("store"):
+                    pkv.store(t.k_new(layer), t.v_new(layer), kc, vc, dm["slot_mapping"])
+            else:
+                pkv.store(t.k_new(layer), t.v_new(layer), kc, vc, dm["slot_mapping"])
+            if plan.kind == "decode":
+                args = (t.q[layer], kc, vc, dm["block_tables"], dm["context_lens"], scale)
+                kw = dict(out=outs[i % pools], workspace=ws)
+                if timed:
+                    with timer.span("attn"):
+                        pkv.decode(*args, **kw)
+                else:
+                    pkv.decode(*args, **kw)
+            else:
+                args = (t.q[layer], kc, vc, dm["block_tables"], dm["cu_seqlens_q"],
+                        dm["cu_seqlens_k"], dm["max_seqlen_q"], dm["max_seqlen_k"], scale)
+                if timed:
+                    with timer.span("attn"):
+                        pkv.prefill_varlen(*args)
+                else:
+                    pkv.prefill_varlen(*args)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - start
+    ms_step = wall * 1e3 / steps
+    res = dict(plan=plan, ms_per_step=ms_step, attn_ms=timer.mean_ms("attn"),
+               store_ms=timer.mean_ms("store"))
+    del tens, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name, budget_s, log):
+    """The oracle (as it stands) on the same workload: one full step (store +
+    attention) repeated until about budget_s of CPU work, inputs on the host."""
+    import torch
+
+    import oracle as O
+    from workloads import make_plan, make_tensors
+
+    plan = make_plan(name)
+    tens = make_tensors(plan, "cpu", poison=False)
+    orc = O.default()
+    om = O.prepare_decode(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    scale = 1.0 / math.sqrt(plan.d)
+    reps, total = 0, 0.0
+    while total < budget_s and reps < 50:
+        kc, vc = tens.k_cache().clone(), tens.v_cache().clone()
+        t0 = time.perf_counter()
+        orc.store(kc, vc, tens.k_new(), tens.v_new(), om["slot_mapping"])
+        orc.decode(tens.q[0], kc, vc, om["block_tables"], om["context_lens"], scale)
+        total += time.perf_counter() - t0
+        reps += 1
+    step_s = total / reps
+    gbs = (decode_bytes(plan) + store_bytes(plan)) / step_s / 1e9
+    log(f"cpu oracle: {reps} full steps of {name}, {step_s * 1e3:.1f} ms each, {orc.threads()} threads")
+    return dict(value=round(gbs, 3), unit="GB/s", cores=orc.threads(), kind="oracle",
+                sample=f"{reps} full {name} steps (store + decode of all {plan.B} sequences), "
+                       f"float64 C oracle, {step_s * 1e3:.1f} ms per step",
+                ms_per_step=round(step_s * 1e3, 2))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_decode",
+                    choices=["qwen3_decode", "long_decode", "prefix_prefill", "full_step"])
+    ap.add_argument("--pools", type=int, default=2,
+                    help="independent copies of the cache rotated across steps (single-layer workloads)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this path has no "
+              "multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_110_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pkv._lib.load()
+
+    def summarize(res):
+        plan = res["plan"]
+        out = dict(workload=plan.name, ms_per_step=round(res["ms_per_step"], 4),
+                   attn_ms=round(res["attn_ms"], 4), store_ms=round(res["store_ms"], 4))
+        if plan.kind == "decode":
+            db = decode_bytes(plan) * plan.layers
+            sb = store_bytes(plan) * plan.layers
+            out["gb_per_s"] = round((db + sb) / (res["ms_per_step"] * 1e-3) / 1e9, 2)
+            out["decode_gb_per_s"] = round(decode_bytes(plan) / (res["attn_ms"] * 1e-3) / 1e9, 2)
+            out["decode_pct_hbm_peak"] = round(100 * out["decode_gb_per_s"] / HBM_PEAK_GBS, 2)
+            out["tokens_per_s"] = round(plan.B / (res["ms_per_step"] * 1e-3), 1)
+            out["kv_tokens_per_layer"] = plan.kv_tokens()
+        else:
+            fl = prefill_flops(plan)
+            out["prefill_tflops"] = round(fl / (res["attn_ms"] * 1e-3) / 1e12, 2)
+            out["prefill_pct_mfma_peak"] = round(100 * out["prefill_tflops"] / BF16_PEAK_TFLOPS, 2)
+            out["tokens_per_s"] = round(plan.total_new / (res["ms_per_step"] * 1e-3), 1)
+            out["flops"] = fl
+        return out
+
+    main_res = run_workload(args.workload, args.steps, args.warmup,
+                            args.pools if args.workload != "full_step" else 1, torch, pkv, log)
+    plan = main_res["plan"]
+    s = summarize(main_res)
+    log(json.dumps(s))
+
+    secondary = {}
+    if not args.no_secondary:
+        for name in ["long_decode", "prefix_prefill", "full_step"]:
+            if name == args.workload:
+                continue
+            r = run_workload(name, max(5, args.steps // 2), 2,
+                             1 if name in ("full_step", "prefix_prefill") else args.pools,
+                             torch, pkv, log)
+            secondary[name] = summarize(r)
+            log(json.dumps(secondary[name]))
+
+    if plan.kind == "decode":
+        value = s["gb_per_s"]
+        unit = "GB/s"
+        per_launch = decode_bytes(plan)
+        achieved = per_launch / (main_res["attn_ms"] * 1e-3) / 1e9
+        roofline = dict(bound="hbm", kernel="pkv_decode (decode_split_kernel + decode_merge_kernel)",
+                        achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        bytes_per_launch=per_launch, avg_launch_ms=round(main_res["attn_ms"], 4))
+    else:
+        value = s["prefill_tflops"]
+        unit = "TFLOP/s"
+        fl = prefill_flops(plan)
+        achieved = fl / (main_res["attn_ms"] * 1e-3) / 1e12
+        roofline = dict(bound="mfma", kernel="prefill_kernel", achieved=round(achieved, 2),
+                        peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                        flops_per_launch=fl, avg_launch_ms=round(main_res["attn_ms"], 4))
+
+    cpu = None
+    if not args.no_cpu_baseline and plan.kind == "decode" and args.workload != "full_step":
+        cpu = cpu_baseline(args.workload, args.cpu_budget, log)
+
+    config = dict(workload=plan.name, B=plan.B, H_q=plan.H_q, H_kv=plan.H_kv, d=plan.d,
+                  block_size=plan.block_size, layers=plan.layers, num_blocks=plan.num_blocks,
+                  kv_tokens=plan.kv_tokens(), new_tokens=plan.total_new,
+                  pools_rotated=args.pools if args.workload != "full_step" else 1,
+                  step="store + attention" + (" per layer" if plan.layers > 1 else ""))
+    line = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps,
+                warmup=args.warmup, ms_per_step=s["ms_per_step"], higher_is_better=True,
+                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                config=config, roofline=roofline, cpu_baseline=cpu, detail=s,
+                secondary=secondary)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

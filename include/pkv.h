@@ -1,0 +1,188 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a block-paged KV cache on AMD
+ * MI355X (gfx950).
+ *
+ * The calls follow the problem as the source pages state it:
+ *  - devpress.csdn.net "nano-vllm解读", section "PagedAttention是如何实现的":
+ *    the decode call's arguments (q as [reqs, H, d]; k_cache/v_cache as
+ *    [max_blocks, block_size, H_kv, d]; int32 cache lengths; an int32
+ *    [reqs, max_len_blocks] block table right-padded with -1;
+ *    softmax_scale = 1/sqrt(d)), and the store kernel that writes each new
+ *    token's K/V at the row slot_mapping[i] of the cache viewed as
+ *    [num_blocks * block_size, H_kv * d];
+ *  - the same page, section "如何适配不同请求不同序列长度": varlen causal
+ *    prefill with queries stacked along the token axis and addressed by
+ *    cumulative lengths cu_seqlens_q / cu_seqlens_k (+ max_seqlen_q/k);
+ *  - caomaolufei.github.io AIInfraGuide 3.6, section 2 ("prepare_prefill /
+ *    prepare_decode"): how slot_mapping, context_lens (the stored token
+ *    included), cu_seqlens and the -1-padded block tables are built, and
+ *    that a slot of -1 writes nothing; section 4: one pool
+ *    [2, layers, num_blocks, block_size, H_kv, d] whose per-layer slices are
+ *    the k_cache/v_cache arguments.
+ *
+ * Conventions shared by every call:
+ *  - bf16 tensors are passed as device pointers to raw 16-bit bfloat16 data,
+ *    16-byte aligned, in the row-major layouts stated per call.
+ *  - Grouped-query attention: query head h reads KV head h / (H_q / H_kv)
+ *    (contiguous groups).  The pages give K/V H_kv heads but do not state the
+ *    grouping; this is the reading used on both sides of every parity test.
+ *  - The caller owns all memory.  The library never allocates, frees or
+ *    synchronises: every device call only enqueues work on `stream` and
+ *    returns.  Calls on one stream run in order, so a store followed by an
+ *    attention call on the same stream sees the stored rows.
+ *  - Errors are reported by the return code only.  Scalar arguments are
+ *    checked on the host before anything is enqueued.  Device-resident
+ *    metadata (slots, block ids, lengths, cu_seqlens) cannot be checked
+ *    without a synchronisation; the kernels clamp or skip out-of-range values
+ *    so that no access leaves the caller's buffers, but the results of such
+ *    calls are unspecified.  Preconditions: every block id a read key maps to
+ *    lies in [0, num_blocks); non-(-1) slots lie in [0, num_blocks*block_size)
+ *    and are unique; context_lens[b] <= max_blocks_per_seq * block_size;
+ *    cu_seqlens are non-decreasing with 0 <= nq <= nk per sequence.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,       /* an argument violates a documented constraint */
+  PKV_EUNSUPPORTED = 2, /* valid, but not a shape this build has kernels for */
+  PKV_ELAUNCH = 3       /* the HIP runtime reported an error at launch */
+} pkv_status;
+
+/* Static, human-readable name of a status code. */
+const char* pkv_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pkv_version(void);
+
+/*
+ * Host metadata for one attention step (AIInfraGuide 3.6, section 2).
+ *
+ * Input, per sequence b (host memory):
+ *   num_cached[b]   tokens already in the cache (c)
+ *   num_new[b]      tokens this step stores and queries (n; 1 for decode)
+ *   block_offsets   [B+1] CSR offsets into block_ids
+ *   block_ids       physical block ids of sequence b in logical order at
+ *                   block_ids[block_offsets[b] .. block_offsets[b+1])
+ * Output (host memory, caller-allocated):
+ *   slot_mapping    [sum n]  slot of new token i of sequence b: position
+ *                   p = c + i, slot = block_ids_b[p / block_size] * block_size
+ *                   + p % block_size
+ *   context_lens    [B]      c + n
+ *   cu_seqlens_q    [B+1]    prefix sums of n
+ *   cu_seqlens_k    [B+1]    prefix sums of c + n
+ *   block_tables    [B, max_blocks_per_seq]  ids, right-padded with -1
+ *   max_seqlen_q, max_seqlen_k   maxima of n and c + n (0 when B == 0)
+ * PKV_EINVAL: B < 0; a null pointer (with B > 0); block_size not a power of
+ * two >= 16; c or n negative; fewer blocks than ceil((c+n)/block_size) or
+ * more than max_blocks_per_seq; a negative block id; int32 overflow of a sum.
+ * Outputs are unspecified after an error.
+ */
+pkv_status pkv_prepare_metadata(int32_t B, const int32_t* num_cached, const int32_t* num_new,
+                                const int32_t* block_offsets, const int32_t* block_ids,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t* slot_mapping, int32_t* context_lens,
+                                int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                                int32_t* block_tables, int32_t* max_seqlen_q,
+                                int32_t* max_seqlen_k);
+
+/*
+ * Store (devpress page, KV-cache write): for i in [0, num_tokens) with
+ * slot_mapping[i] != -1, copy the H_kv*d bf16 values of key[i] and value[i]
+ * bit for bit to row slot_mapping[i] of k_cache and v_cache.
+ *   key, value   device, [num_tokens, H_kv, d] bf16; head and d contiguous,
+ *                token stride key_stride / value_stride elements (>= H_kv*d,
+ *                multiple of 8), e.g. views into a fused QKV projection.
+ *   k_cache, v_cache   device, [num_blocks, block_size, H_kv, d] bf16, contiguous.
+ *   slot_mapping device, [num_tokens] int32; -1 = padding, nothing written.
+ * Slots outside [-1, num_blocks*block_size) are skipped by the kernel.
+ * num_tokens == 0 enqueues nothing and returns PKV_OK.
+ * PKV_EINVAL: null pointers (num_tokens > 0), num_tokens < 0, non-positive
+ * sizes, block_size not a power of two >= 16, a stride below H_kv*d or not a
+ * multiple of 8, pointers not 16-byte aligned, int64 overflow of the pool size.
+ */
+pkv_status pkv_store(const void* key, int64_t key_stride, const void* value,
+                     int64_t value_stride, void* k_cache, void* v_cache,
+                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                     int32_t block_size, int32_t H_kv, int32_t d, hipStream_t stream);
+
+/*
+ * Bytes of device workspace pkv_decode needs for these sizes (split-K partial
+ * results: one (max, sum, d-vector) triple of fp32 per query head and per
+ * split).  0 for invalid sizes.
+ */
+size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
+                                 int32_t block_size, int32_t max_blocks_per_seq);
+
+/*
+ * Paged decode attention (devpress page, "PagedAttention是如何实现的";
+ * AIInfraGuide 3.6, section 2):
+ *   out[b, h, :] = softmax_j( q[b,h,:] . K_b[j, h/G, :] * softmax_scale ) V_b[j, h/G, :]
+ * over j in [0, context_lens[b]), where key j of sequence b is row
+ * j % block_size of physical block block_tables[b][j / block_size].
+ *   out, q        device, [B, H_q, d] bf16, contiguous (out rounded to nearest even)
+ *   k_cache, v_cache   device, [num_blocks, block_size, H_kv, d] bf16, contiguous
+ *   block_tables  device, [B, max_blocks_per_seq] int32, -1 padded (never read)
+ *   context_lens  device, [B] int32, the just-stored token included; 0 gives a
+ *                 zero output row; values above max_blocks_per_seq*block_size
+ *                 are clamped to it
+ *   workspace     device, >= pkv_decode_workspace_size(...) bytes, 16-byte
+ *                 aligned; contents on entry are irrelevant and unspecified on
+ *                 return; may be NULL when the size query returns 0
+ * The causal mask of the pages' call is a no-op for one query per sequence.
+ * Long contexts are split over the KV sequence and merged with a log-sum-exp
+ * rescale; split boundaries depend only on the host sizes, so results are
+ * deterministic run to run.
+ * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, block_size
+ * not a power of two >= 16, misaligned pointers, too small a workspace.
+ * PKV_EUNSUPPORTED: d not in {64, 128} or H_q/H_kv not in {1, 2, 4, 8}.
+ */
+pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                      int32_t H_q, int32_t H_kv, int32_t d, int32_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Varlen causal prefill over the paged cache (devpress page, "如何适配不同请求
+ * 不同序列长度"; AIInfraGuide 3.6, section 2).  Sequence b has
+ * nq = cu_seqlens_q[b+1]-cu_seqlens_q[b] new queries and
+ * nk = cu_seqlens_k[b+1]-cu_seqlens_k[b] keys, c = nk - nq of them cached.
+ * Query i of sequence b sits at absolute position c + i and attends keys
+ * 0 .. c + i (causal, bottom-right aligned), read through block_tables[b]:
+ *   out[cu_q[b]+i, h, :] = softmax_j<=c+i( q . K_b[j, h/G] * scale ) V_b[j, h/G]
+ * Only the differences of cu_seqlens_k are used: keys always come from the cache,
+ * so the new tokens' K/V must have been stored first (pkv_store, same stream).
+ *   out, q        device, [total_q, H_q, d] bf16, contiguous; total_q = cu_seqlens_q[B]
+ *   cu_seqlens_q, cu_seqlens_k   device, [B+1] int32, cu_seqlens_q[0] == 0
+ *   max_seqlen_q  host bound on nq (sizes the grid; sequences beyond it are cut)
+ *   max_seqlen_k  host bound on nk (informational; keys are clamped to the table)
+ *   other arguments as for pkv_decode.
+ * Query rows at or beyond total_q are never written.
+ * PKV_EINVAL / PKV_EUNSUPPORTED as for pkv_decode, plus total_q < 0 or
+ * max_seqlen_q < 0.  B == 0 or max_seqlen_q == 0 enqueues nothing.
+ */
+pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t B, int32_t total_q, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t H_q, int32_t H_kv, int32_t d,
+                              int32_t num_blocks, int32_t block_size,
+                              int32_t max_blocks_per_seq, float softmax_scale,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -72,6 +72,7 @@ def _load(plant: int = 0) -> ctypes.CDLL:
     for fn in (lib.pkv_oracle_store, lib.pkv_oracle_decode, lib.pkv_oracle_prefill):
         fn.restype = ctypes.c_int
     lib.pkv_oracle_plant.restype = ctypes.c_int
+    lib.pkv_oracle_threads.restype = ctypes.c_int
     _LIBS[plant] = lib
     return lib
 
@@ -98,6 +99,10 @@ class Oracle:
     def __init__(self, plant: int = 0):
         self.plant = plant
         self.lib = _load(plant)
+
+    def threads(self) -> int:
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self.lib.pkv_oracle_threads())
 
     # -- store --------------------------------------------------------------
     def store(self, k_cache: torch.Tensor, v_cache: torch.Tensor, key: torch.Tensor,

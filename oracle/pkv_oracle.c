@@ -37,6 +37,9 @@
  * default build (PKV_ORACLE_PLANT undefined or 0) has none.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -63,6 +66,15 @@ static double widen_bf16(uint16_t bits) {
 }
 
 int pkv_oracle_plant(void) { return PKV_ORACLE_PLANT; }
+
+/* Threads the parallel loops below use (OpenMP's current maximum). */
+int pkv_oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ store */
 int pkv_oracle_store(uint16_t* k_cache, uint16_t* v_cache,

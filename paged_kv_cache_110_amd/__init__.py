@@ -1,0 +1,179 @@
+"""Paged-KV attention for AMD MI355X (gfx950): Python binding of libpkv.
+
+Thin marshalling over the C ABI in include/pkv.h: every function checks the
+torch tensors it is given (device, dtype, shape, contiguity), turns them into
+raw pointers and sizes, and calls the library on the current HIP stream.  All
+computation happens in the library's kernels (or, for ``prepare_metadata``,
+in its host routine).  Output and workspace tensors are allocated with torch
+when the caller does not pass them.
+
+Functions:
+    prepare_metadata(seqs, block_size, max_blocks_per_seq) -> dict (host int32 tensors)
+    store(key, value, k_cache, v_cache, slot_mapping)
+    decode(q, k_cache, v_cache, block_tables, context_lens, softmax_scale=None, ...)
+    prefill_varlen(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
+                   max_seqlen_q, max_seqlen_k, softmax_scale=None, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from ._lib import EXPORTS, LIB_PATH, PkvError, check, load
+
+__all__ = [
+    "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
+    "PkvError", "LIB_PATH", "EXPORTS", "version",
+]
+
+
+def version() -> int:
+    return load().pkv_version()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev_i32(t: torch.Tensor, name: str) -> None:
+    _need(t.is_cuda and t.dtype == torch.int32 and t.is_contiguous(),
+          f"{name} must be a contiguous int32 GPU tensor")
+
+
+def _cache_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape,
+          "k_cache/v_cache must both be [num_blocks, block_size, H_kv, d]")
+    _need(k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16,
+          "caches must be bfloat16")
+    _need(k_cache.is_cuda and v_cache.is_cuda, "caches must be GPU tensors")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "caches must be contiguous")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def prepare_metadata(seqs: Sequence, block_size: int, max_blocks_per_seq: int) -> dict:
+    """Host metadata of one step from per-sequence block-manager state.
+
+    ``seqs``: objects with ``block_ids`` (physical ids, logical order),
+    ``num_cached`` and ``num_new``.  Returns CPU int32 tensors ``slot_mapping``,
+    ``context_lens``, ``cu_seqlens_q``, ``cu_seqlens_k``, ``block_tables`` and
+    the ints ``max_seqlen_q``/``max_seqlen_k``.
+    """
+    lib = load()
+    B = len(seqs)
+    cached = torch.tensor([s.num_cached for s in seqs], dtype=torch.int32)
+    new = torch.tensor([s.num_new for s in seqs], dtype=torch.int32)
+    offs = [0]
+    for s in seqs:
+        offs.append(offs[-1] + len(s.block_ids))
+    offsets = torch.tensor(offs, dtype=torch.int32)
+    ids = torch.tensor([b for s in seqs for b in s.block_ids] or [0], dtype=torch.int32)
+    total_new = int(new.sum()) if B else 0
+    slot = torch.empty(max(total_new, 1), dtype=torch.int32)
+    ctx = torch.empty(max(B, 1), dtype=torch.int32)
+    cu_q = torch.empty(B + 1, dtype=torch.int32)
+    cu_k = torch.empty(B + 1, dtype=torch.int32)
+    bt = torch.empty(max(B * max_blocks_per_seq, 1), dtype=torch.int32)
+    mq, mk = ctypes.c_int32(0), ctypes.c_int32(0)
+    check("pkv_prepare_metadata", lib.pkv_prepare_metadata(
+        B, _ptr(cached), _ptr(new), _ptr(offsets), _ptr(ids), block_size, max_blocks_per_seq,
+        _ptr(slot), _ptr(ctx), _ptr(cu_q), _ptr(cu_k), _ptr(bt), ctypes.byref(mq),
+        ctypes.byref(mk)))
+    return dict(
+        slot_mapping=slot[:total_new], context_lens=ctx[:B], cu_seqlens_q=cu_q,
+        cu_seqlens_k=cu_k, block_tables=bt[: B * max_blocks_per_seq].view(B, max_blocks_per_seq),
+        max_seqlen_q=mq.value, max_seqlen_k=mk.value,
+    )
+
+
+def store(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+          slot_mapping: torch.Tensor, stream=None) -> None:
+    """k_cache/v_cache row slot_mapping[i] <- key[i]/value[i]; slot -1 is skipped."""
+    nb, bs, H_kv, d = _cache_geometry(k_cache, v_cache)
+    _need(key.dim() == 3 and key.shape == value.shape and tuple(key.shape[1:]) == (H_kv, d),
+          "key/value must be [N, H_kv, d] matching the cache")
+    _need(key.dtype == torch.bfloat16 and value.dtype == torch.bfloat16, "key/value bfloat16")
+    _need(key.is_cuda and value.is_cuda, "key/value must be GPU tensors")
+    _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1
+          and value.stride(1) == d, "key/value head and d dims must be contiguous")
+    _dev_i32(slot_mapping, "slot_mapping")
+    N = key.shape[0]
+    _need(slot_mapping.shape == (N,), "slot_mapping must be [N]")
+    check("pkv_store", load().pkv_store(
+        _ptr(key), key.stride(0), _ptr(value), value.stride(0), _ptr(k_cache), _ptr(v_cache),
+        _ptr(slot_mapping), N, nb, bs, H_kv, d, _stream(stream)))
+
+
+def decode_workspace_size(B: int, H_q: int, H_kv: int, d: int, block_size: int,
+                          max_blocks_per_seq: int) -> int:
+    return int(load().pkv_decode_workspace_size(B, H_q, H_kv, d, block_size, max_blocks_per_seq))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor,
+           softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged decode attention; q [B, H_q, d] -> out [B, H_q, d] (bf16)."""
+    nb, bs, H_kv, d = _cache_geometry(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == torch.bfloat16 and q.is_cuda
+          and q.is_contiguous(), "q must be a contiguous bf16 GPU tensor [B, H_q, d]")
+    B, H_q = int(q.shape[0]), int(q.shape[1])
+    _dev_i32(block_tables, "block_tables")
+    _dev_i32(context_lens, "context_lens")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, maxb]")
+    _need(context_lens.shape == (B,), "context_lens must be [B]")
+    maxb = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    ws_bytes = decode_workspace_size(B, H_q, H_kv, d, bs, maxb)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    check("pkv_decode", load().pkv_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        B, H_q, H_kv, d, nb, bs, maxb, scale, _ptr(workspace), have, _stream(stream)))
+    return out
+
+
+def prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                   cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                   softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Varlen causal prefill over the paged cache; q [total_q, H_q, d] -> out (bf16)."""
+    nb, bs, H_kv, d = _cache_geometry(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == torch.bfloat16 and q.is_cuda
+          and q.is_contiguous(), "q must be a contiguous bf16 GPU tensor [total_q, H_q, d]")
+    total_q, H_q = int(q.shape[0]), int(q.shape[1])
+    _dev_i32(block_tables, "block_tables")
+    _dev_i32(cu_seqlens_q, "cu_seqlens_q")
+    _dev_i32(cu_seqlens_k, "cu_seqlens_k")
+    B = int(cu_seqlens_q.shape[0]) - 1
+    _need(cu_seqlens_k.shape == cu_seqlens_q.shape and B >= 0, "cu_seqlens must be [B+1]")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, maxb]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    check("pkv_prefill_varlen", load().pkv_prefill_varlen(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), B, total_q, int(max_seqlen_q), int(max_seqlen_k), H_q, H_kv, d, nb, bs,
+        int(block_tables.shape[1]), scale, _stream(stream)))
+    return out

@@ -1,0 +1,71 @@
+"""ctypes loader for libpkv.so (the C ABI declared in include/pkv.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation anywhere in the package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, 1, 2, 3
+
+# every symbol include/pkv.h declares
+EXPORTS = (
+    "pkv_status_string",
+    "pkv_version",
+    "pkv_prepare_metadata",
+    "pkv_store",
+    "pkv_decode_workspace_size",
+    "pkv_decode",
+    "pkv_prefill_varlen",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_110_amd.build` "
+            "(hipcc, gfx950). There is no CPU fallback."
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                          ctypes.c_size_t)
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_prepare_metadata.argtypes = [I32, P, P, P, P, I32, I32, P, P, P, P, P, P, P]
+    lib.pkv_prepare_metadata.restype = ctypes.c_int
+    lib.pkv_store.argtypes = [P, I64, P, I64, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_store.restype = ctypes.c_int
+    lib.pkv_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pkv_decode_workspace_size.restype = SZ
+    lib.pkv_decode.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, SZ, P]
+    lib.pkv_decode.restype = ctypes.c_int
+    lib.pkv_prefill_varlen.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
+                                       I32, I32, I32, F, P]
+    lib.pkv_prefill_varlen.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != PKV_OK:
+        msg = load().pkv_status_string(status).decode()
+        raise PkvError(fn, status, msg)

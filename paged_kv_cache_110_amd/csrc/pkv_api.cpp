@@ -1,0 +1,186 @@
+// C ABI of libpkv: argument checks on the host, then kernel launches.
+// Declarations and the full contract are in include/pkv.h.
+#include "pkv.h"
+
+#include <limits.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_ge16(int32_t x) { return x >= 16 && (x & (x - 1)) == 0; }
+
+bool supported_d(int32_t d) { return d == 64 || d == 128; }
+
+bool supported_group(int32_t H_q, int32_t H_kv) {
+  const int32_t g = H_q / H_kv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+// Checks shared by the two attention calls.
+pkv_status check_attention(const void* out, const void* q, const void* k_cache,
+                           const void* v_cache, const void* block_tables, int32_t H_q,
+                           int32_t H_kv, int32_t d, int32_t num_blocks, int32_t block_size,
+                           int32_t max_blocks_per_seq) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables) return PKV_EINVAL;
+  if (H_q <= 0 || H_kv <= 0 || d <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PKV_EINVAL;
+  if (H_q % H_kv != 0 || !pow2_ge16(block_size)) return PKV_EINVAL;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return PKV_EINVAL;
+  if ((int64_t)num_blocks * block_size > INT32_MAX) return PKV_EINVAL;  // slots are int32
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_EINVAL;
+  if (!supported_d(d) || !supported_group(H_q, H_kv)) return PKV_EUNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
+    case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: unsupported head size or group size";
+    case PKV_ELAUNCH: return "PKV_ELAUNCH: kernel launch failed";
+    default: return "unknown pkv status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+pkv_status pkv_prepare_metadata(int32_t B, const int32_t* num_cached, const int32_t* num_new,
+                                const int32_t* block_offsets, const int32_t* block_ids,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t* slot_mapping, int32_t* context_lens,
+                                int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                                int32_t* block_tables, int32_t* max_seqlen_q,
+                                int32_t* max_seqlen_k) {
+  if (B < 0 || !pow2_ge16(block_size) || max_blocks_per_seq < 0) return PKV_EINVAL;
+  if (!cu_seqlens_q || !cu_seqlens_k || !max_seqlen_q || !max_seqlen_k) return PKV_EINVAL;
+  if (B > 0 && (!num_cached || !num_new || !block_offsets || !context_lens ||
+                (max_blocks_per_seq > 0 && !block_tables)))
+    return PKV_EINVAL;
+  int shift = 0;
+  while ((1 << shift) < block_size) ++shift;
+  const int32_t mask = block_size - 1;
+  int64_t cq = 0, ck = 0;
+  int32_t mq = 0, mk = 0;
+  cu_seqlens_q[0] = 0;
+  cu_seqlens_k[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t c = num_cached[b], n = num_new[b];
+    if (c < 0 || n < 0 || c + n > INT32_MAX) return PKV_EINVAL;
+    const int64_t lo = block_offsets[b], hi = block_offsets[b + 1];
+    const int64_t owned = hi - lo;
+    const int64_t needed = (c + n + block_size - 1) >> shift;
+    if (lo < 0 || owned < needed || owned > max_blocks_per_seq) return PKV_EINVAL;
+    if (owned > 0 && !block_ids) return PKV_EINVAL;
+    int32_t* row = block_tables + (int64_t)b * max_blocks_per_seq;
+    for (int64_t j = 0; j < max_blocks_per_seq; ++j) {
+      int32_t id = -1;
+      if (j < owned) {
+        id = block_ids[lo + j];
+        if (id < 0 || (int64_t)id * block_size + mask > INT32_MAX) return PKV_EINVAL;
+      }
+      row[j] = id;
+    }
+    if (n > 0 && !slot_mapping) return PKV_EINVAL;
+    for (int64_t p = c; p < c + n; ++p)  // position p of the sequence
+      slot_mapping[cq + (p - c)] = row[p >> shift] * block_size + (int32_t)(p & mask);
+    cq += n;
+    ck += c + n;
+    if (cq > INT32_MAX || ck > INT32_MAX) return PKV_EINVAL;
+    cu_seqlens_q[b + 1] = (int32_t)cq;
+    cu_seqlens_k[b + 1] = (int32_t)ck;
+    context_lens[b] = (int32_t)(c + n);
+    if (n > mq) mq = (int32_t)n;
+    if (c + n > mk) mk = (int32_t)(c + n);
+  }
+  *max_seqlen_q = mq;
+  *max_seqlen_k = mk;
+  return PKV_OK;
+}
+
+pkv_status pkv_store(const void* key, int64_t key_stride, const void* value,
+                     int64_t value_stride, void* k_cache, void* v_cache,
+                     const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                     int32_t block_size, int32_t H_kv, int32_t d, hipStream_t stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || H_kv <= 0 || d <= 0 || !pow2_ge16(block_size))
+    return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_EINVAL;
+  const int64_t row = (int64_t)H_kv * d;
+  if (row % 8 != 0 || row > INT32_MAX / 2) return PKV_EINVAL;
+  if (key_stride < row || value_stride < row || key_stride % 8 || value_stride % 8)
+    return PKV_EINVAL;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_EINVAL;
+  const int64_t slots = (int64_t)num_blocks * block_size;
+  if (slots > INT64_MAX / row) return PKV_EINVAL;
+  return launch_status(pkv::launch_store(
+      static_cast<const uint16_t*>(key), key_stride, static_cast<const uint16_t*>(value),
+      value_stride, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+      slot_mapping, num_tokens, slots, (int32_t)row, stream));
+}
+
+size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
+                                 int32_t block_size, int32_t max_blocks_per_seq) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || d <= 0 || max_blocks_per_seq <= 0 ||
+      !pow2_ge16(block_size) || H_q % H_kv != 0)
+    return 0;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return 0;
+  return pkv::decode_plan(B, H_q, H_kv, d, block_size, max_blocks_per_seq).workspace_bytes;
+}
+
+pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                      int32_t H_q, int32_t H_kv, int32_t d, int32_t num_blocks,
+                      int32_t block_size, int32_t max_blocks_per_seq, float softmax_scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B <= 0 || !context_lens) return PKV_EINVAL;
+  pkv_status st = check_attention(out, q, k_cache, v_cache, block_tables, H_q, H_kv, d,
+                                  num_blocks, block_size, max_blocks_per_seq);
+  if (st != PKV_OK) return st;
+  if ((int64_t)B * H_kv > INT32_MAX) return PKV_EINVAL;
+  const pkv::DecodePlan plan = pkv::decode_plan(B, H_q, H_kv, d, block_size, max_blocks_per_seq);
+  if (plan.num_splits > 65535) return PKV_EINVAL;
+  if (plan.workspace_bytes > 0 &&
+      (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace)))
+    return PKV_EINVAL;
+  return launch_status(pkv::launch_decode(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_tables,
+      context_lens, B, H_q, H_kv, d, num_blocks, block_size, max_blocks_per_seq, softmax_scale,
+      workspace, plan, stream));
+}
+
+pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t B, int32_t total_q, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t H_q, int32_t H_kv, int32_t d,
+                              int32_t num_blocks, int32_t block_size,
+                              int32_t max_blocks_per_seq, float softmax_scale,
+                              hipStream_t stream) {
+  (void)max_seqlen_k;
+  if (B < 0 || total_q < 0 || max_seqlen_q < 0) return PKV_EINVAL;
+  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return PKV_OK;
+  if (!cu_seqlens_q || !cu_seqlens_k) return PKV_EINVAL;
+  pkv_status st = check_attention(out, q, k_cache, v_cache, block_tables, H_q, H_kv, d,
+                                  num_blocks, block_size, max_blocks_per_seq);
+  if (st != PKV_OK) return st;
+  if (B > 65535) return PKV_EINVAL;
+  return launch_status(pkv::launch_prefill(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_tables,
+      cu_seqlens_q, cu_seqlens_k, B, total_q, max_seqlen_q, H_q, H_kv, d, num_blocks, block_size,
+      max_blocks_per_seq, softmax_scale, stream));
+}
+
+}  // extern "C"

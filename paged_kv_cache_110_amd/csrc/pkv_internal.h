@@ -1,0 +1,39 @@
+// Internal launchers between the C-ABI layer (pkv_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Store: one thread per 16-byte chunk of a K or V row.
+hipError_t launch_store(const uint16_t* key, int64_t key_stride, const uint16_t* value,
+                        int64_t value_stride, uint16_t* k_cache, uint16_t* v_cache,
+                        const int32_t* slot_mapping, int32_t num_tokens, int64_t num_slots,
+                        int32_t row_elems, hipStream_t stream);
+
+// Decode split plan: tokens per split and number of splits for the sizes.
+struct DecodePlan {
+  int32_t split_tokens;  // multiple of the kernel's tile length
+  int32_t num_splits;    // ceil(max_blocks_per_seq * block_size / split_tokens)
+  size_t workspace_bytes;
+};
+DecodePlan decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t block_size,
+                       int32_t max_blocks_per_seq);
+
+hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                         const uint16_t* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv,
+                         int32_t d, int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
+                         const DecodePlan& plan, hipStream_t stream);
+
+hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                          const uint16_t* v_cache, const int32_t* block_tables,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t B,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t H_q, int32_t H_kv,
+                          int32_t d, int32_t num_blocks, int32_t block_size,
+                          int32_t max_blocks_per_seq, float softmax_scale, hipStream_t stream);
+
+}  // namespace pkv

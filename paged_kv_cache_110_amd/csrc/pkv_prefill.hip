@@ -1,0 +1,319 @@
+// Varlen causal prefill over the paged KV cache on MFMA.
+//
+// What is computed (devpress "nano-vllm解读", "如何适配不同请求不同序列长度";
+// AIInfraGuide 3.6, section 2): sequence b has nq new queries and nk keys,
+// c = nk - nq of them cached; query i sits at position c + i and attends keys
+// 0 .. c + i of the sequence, read through its block table.  Grouped-query:
+// query head h reads KV head h / G.
+//
+// How (MI355X, gfx950): a dense contraction, so both products run on MFMA
+// (v_mfma_f32_32x32x16_bf16, bf16 in, fp32 accumulate):
+//  - a workgroup (4 wavefronts) owns one KV head, one sequence and a tile of
+//    query positions; its M dimension packs (query position, head of the
+//    group) pairs, 32 per wavefront, so all G heads share every K/V tile;
+//  - K/V tiles of 64 keys are gathered through the block table (per-row
+//    lookup, so any power-of-two block size works) into LDS, double-buffered,
+//    the next tile's global loads in flight while the current tile computes.
+//    Rows are stored with a 16-byte-chunk XOR swizzle chosen so that both
+//    the K operand reads (one row per lane) and the V transpose reads (four
+//    rows per 16 lanes) hit distinct banks;
+//  - S^T = K Q^T puts keys on the MFMA M side and the packed query rows on N,
+//    so every lane ends up owning scores of a single query row: the softmax
+//    statistics are per lane (plus one exchange with lane l^32);
+//  - O^T += V^T P^T: the P operand is the lane's own scores (rounded to bf16)
+//    and the V^T operand comes straight from the row-major V tile with
+//    ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit elements;
+//  - online softmax in the log2 domain with the same lazy rescale as decode;
+//    only tiles that cross the diagonal are masked;
+//  - workgroups run the last (most expensive, causally longest) query tiles
+//    of every sequence first.
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kPrefillBN = 64;  // keys per tile
+constexpr float kPrefillLazy = 8.0f;
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// 16-byte chunk swizzle: rows r..r+7 map one logical chunk to 8 distinct
+// chunks, and rows 4k..4k+3 map a pair of adjacent chunks to 8 distinct chunks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  int g = ((row & 3) << 1) | ((row >> 2) & 1);
+  if constexpr (CPR >= 16) g |= (row & 8);
+  return g;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, uint16_t* __restrict__ out,
+    int32_t total_q, int32_t H_kv, int32_t num_blocks, int32_t bs_log2, int32_t maxb,
+    float scale_log2e) {
+  constexpr int BN = kPrefillBN;
+  constexpr int QPW = 32 / G;          // query positions per wavefront
+  constexpr int QPB = 4 * QPW;         // query positions per workgroup
+  constexpr int KS = D / 16;           // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;           // 32-wide d blocks of O^T
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;       // rows per load pass
+  constexpr int PASSES = BN / RPP;     // load passes per tile and tensor
+  constexpr int TILE = BN * D;         // elements per K (or V) tile
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];  // [buf][K|V][BN][D]
+
+  const int h_kv = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int H_q = H_kv * G;
+
+  const int qs = cu_q[b];
+  const int nq = cu_q[b + 1] - qs;
+  const int cap = maxb << bs_log2;
+  int nk = cu_k[b + 1] - cu_k[b];
+  nk = nk > cap ? cap : nk;
+  if (nq <= 0 || nk < nq || qs < 0) return;
+  const int c = nk - nq;
+  const int nqt = (nq + QPB - 1) / QPB;
+  const int qt = nqt - 1 - (int)blockIdx.z;
+  if (qt < 0) return;
+  const int q0 = qt * QPB;
+  const int kend = min(nk, c + q0 + QPB);
+  const int ntiles = (kend + BN - 1) / BN;
+
+  // this lane's query row (one of the 32 packed rows of the wavefront)
+  const int mrow = lane & 31;
+  const int half = lane >> 5;
+  const int qq = q0 + wave * QPW + mrow / G;
+  const int head = h_kv * G + (mrow % G);
+  const bool row_ok = qq < nq && (int64_t)qs + qq < total_q;
+  const int qpos = c + qq;
+  const int wave_first_pos = c + q0 + wave * QPW;
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = q + (((int64_t)qs + qq) * H_q + head) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = row_ok ? ld16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  float m = kNegSentinel;
+  float l = 0.f;
+
+  // cooperative tile loader: thread -> (chunk, rows)
+  const int ch = tid % CPR;
+  const int r0 = tid / CPR;
+  const int64_t row_stride = (int64_t)H_kv * D;
+  const uint16_t* kbase = k_cache + (int64_t)h_kv * D + ch * 8;
+  const uint16_t* vbase = v_cache + (int64_t)h_kv * D + ch * 8;
+  const int32_t* table = block_tables + (int64_t)b * maxb;
+  const int bmask = (1 << bs_log2) - 1;
+
+  u32x4 kr[PASSES], vr[PASSES];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int j = kt * BN + r0 + RPP * p;
+      bool ok = j < kend;
+      const int blk = ok ? table[j >> bs_log2] : 0;
+      ok = ok && (unsigned)blk < (unsigned)num_blocks;
+      if (ok) {
+        const int64_t off = (((int64_t)blk << bs_log2) + (j & bmask)) * row_stride;
+        kr[p] = ld16(kbase + off);
+        vr[p] = ld16(vbase + off);
+      } else {
+        kr[p] = u32x4{0, 0, 0, 0};
+        vr[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto stash_tile = [&](int buf) {
+    uint16_t* kt_lds = lds + buf * 2 * TILE;
+    uint16_t* vt_lds = kt_lds + TILE;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = r0 + RPP * p;
+      const int pc = ch ^ swz<CPR>(r);
+      *reinterpret_cast<u32x4*>(kt_lds + r * D + pc * 8) = kr[p];
+      *reinterpret_cast<u32x4*>(vt_lds + r * D + pc * 8) = vr[p];
+    }
+  };
+
+  load_tile(0);
+  stash_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < ntiles;
+    if (more) load_tile(kt + 1);
+    const uint16_t* kt_lds = lds + buf * 2 * TILE;
+    const uint16_t* vt_lds = kt_lds + TILE;
+
+    // S^T for two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      const int row = kb * 32 + mrow;
+      const int sw = swz<CPR>(row);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int pc = (2 * ks + half) ^ sw;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + row * D + pc * 8);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks],
+                                                           sacc[kb], 0, 0, 0);
+      }
+    }
+
+    // scale, causal mask on diagonal tiles, tile max of this row
+    const bool need_mask = kt * BN + BN - 1 > wave_first_pos;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sv = sacc[kb][r] * scale_log2e;
+        if (need_mask) {
+          const int key = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          sv = key > qpos ? -INFINITY : sv;
+        }
+        sacc[kb][r] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    if (__any(mx > m + kPrefillLazy)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+
+    // P (bf16) in the B-operand layout of O^T += V^T P^T
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(sacc[kb][8 * s2 + e] - m);
+          l += p;
+          pf[kb][s2][e] = (__bf16)p;
+        }
+      }
+    }
+
+    // O^T += V^T P^T, V^T operands by transpose reads of the row-major V tile
+    const int i16 = lane & 15;
+    const int grp16 = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = db * 32 + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      const int chunk = col >> 3;
+      const int sub8 = col & 7;  // 0 or 4 elements into the chunk
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int k0 = kb * 32 + 16 * s2 + 4 * half;
+          const int ra = k0 + (i16 >> 2);
+          const int rb = ra + 8;
+          const i16x4 va = lds_read_tr16(vt_lds + ra * D + ((chunk ^ swz<CPR>(ra)) << 3) + sub8);
+          const i16x4 vb = lds_read_tr16(vt_lds + rb * D + ((chunk ^ swz<CPR>(rb)) << 3) + sub8);
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[kb][s2],
+                                                          o[db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (more) stash_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  l += shfl_xor_f32(l, 32);
+  if (!row_ok) return;
+  const float inv = 1.0f / l;
+  uint16_t* op = out + (((int64_t)qs + qq) * H_q + head) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = db * 32 + 8 * r4 + 4 * half;
+      u32x2 w;
+      w[0] = pack_bf16x2(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
+      w[1] = pack_bf16x2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + d0) = w;
+    }
+  }
+}
+
+static int ilog2p(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+template <int D, int G>
+static void launch_pf(dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* kc,
+                      const uint16_t* vc, const int32_t* bt, const int32_t* cq, const int32_t* ck,
+                      uint16_t* out, int32_t total_q, int32_t H_kv, int32_t nb, int32_t bsl,
+                      int32_t maxb, float sl2e) {
+  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(256), 0, st, q, kc, vc, bt, cq, ck, out,
+                     total_q, H_kv, nb, bsl, maxb, sl2e);
+}
+
+hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                          const uint16_t* v_cache, const int32_t* block_tables,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t B,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t H_q, int32_t H_kv,
+                          int32_t d, int32_t num_blocks, int32_t block_size,
+                          int32_t max_blocks_per_seq, float softmax_scale, hipStream_t stream) {
+  const int G = H_q / H_kv;
+  const int qpb = 4 * (32 / G);
+  const unsigned zt = (unsigned)((max_seqlen_q + qpb - 1) / qpb);
+  dim3 grid((unsigned)H_kv, (unsigned)B, zt);
+  const int bsl = ilog2p(block_size);
+  const float sl2e = softmax_scale * 1.4426950408889634f;
+#define PKV_PF(DD, GG)                                                                       \
+  launch_pf<DD, GG>(grid, stream, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, \
+                    out, total_q, H_kv, num_blocks, bsl, max_blocks_per_seq, sl2e)
+  if (d == 128) {
+    switch (G) {
+      case 1: PKV_PF(128, 1); break;
+      case 2: PKV_PF(128, 2); break;
+      case 4: PKV_PF(128, 4); break;
+      case 8: PKV_PF(128, 8); break;
+    }
+  } else {
+    switch (G) {
+      case 1: PKV_PF(64, 1); break;
+      case 2: PKV_PF(64, 2); break;
+      case 4: PKV_PF(64, 4); break;
+      case 8: PKV_PF(64, 8); break;
+    }
+  }
+#undef PKV_PF
+  return hipGetLastError();
+}
+
+}  // namespace pkv
