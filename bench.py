@@ -166,8 +166,10 @@ def cpu_baseline(name, budget_s, log):
     om = O.prepare_decode(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
     scale = 1.0 / math.sqrt(plan.d)
     reps, total = 0, 0.0
-    while total < budget_s and reps < 50:
-        kc, vc = tens.k_cache().clone(), tens.v_cache().clone()
+    kc, vc = tens.k_cache().clone(), tens.v_cache().clone()
+    while total < budget_s and reps < 1000:
+        # storing the same rows again leaves the cache unchanged, so every
+        # repetition is the same full step
         t0 = time.perf_counter()
         orc.store(kc, vc, tens.k_new(), tens.v_new(), om["slot_mapping"])
         orc.decode(tens.q[0], kc, vc, om["block_tables"], om["context_lens"], scale)
@@ -182,6 +184,32 @@ def cpu_baseline(name, budget_s, log):
                 ms_per_step=round(step_s * 1e3, 2))
 
 
+def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
+    """Plain device copy (torch copy_) and plain read (torch sum) of a buffer of known
+    size: the achievable-bandwidth reference for the roofline, and the known-size
+    kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    n = int(gib * (1 << 30)) // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 4 * n),
+                             ("read", lambda: src.sum(), 2 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / iters
+        res[name] = dict(bytes=nbytes, ms=round(ms, 4), gb_per_s=round(nbytes / ms / 1e6, 1))
+        log(f"{name} probe: {nbytes / 2**30:.2f} GiB in {ms:.3f} ms = {nbytes / ms / 1e6:.0f} GB/s")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +222,8 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the plain copy / read probes and print their JSON")
     args = ap.parse_args()
 
     def log(msg):
@@ -212,6 +242,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     pkv._lib.load()
+    if args.copy_probe:
+        print(json.dumps(dict(probe=copy_probe(torch, log))), flush=True)
+        return 0
 
     def summarize(res):
         plan = res["plan"]

@@ -117,9 +117,11 @@ pkv_status pkv_store(const void* key, int64_t key_stride, const void* value,
                      int32_t block_size, int32_t H_kv, int32_t d, hipStream_t stream);
 
 /*
- * Bytes of device workspace pkv_decode needs for these sizes (split-K partial
- * results: one (max, sum, d-vector) triple of fp32 per query head and per
- * split).  0 for invalid sizes.
+ * Bytes of device workspace pkv_decode needs for these sizes on the current
+ * HIP device: two fp32 partial results (max, sum, d-vector) per query head of
+ * a group for every resident wavefront of the device, plus a 16-byte record
+ * per (sequence, KV head).  Query it with the device current that will run
+ * the decode.  0 for invalid or unsupported sizes.
  */
 size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
                                  int32_t block_size, int32_t max_blocks_per_seq);
@@ -138,11 +140,13 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d
  *                 are clamped to it
  *   workspace     device, >= pkv_decode_workspace_size(...) bytes, 16-byte
  *                 aligned; contents on entry are irrelevant and unspecified on
- *                 return; may be NULL when the size query returns 0
+ *                 return
  * The causal mask of the pages' call is a no-op for one query per sequence.
- * Long contexts are split over the KV sequence and merged with a log-sum-exp
- * rescale; split boundaries depend only on the host sizes, so results are
- * deterministic run to run.
+ * The work (every 16-token tile of every (sequence, KV head)) is split evenly
+ * over one wavefront per resident slot of the device; pieces of a sequence
+ * that straddle wavefronts are merged with a log-sum-exp rescale in a second
+ * kernel.  The split depends only on the context lengths and the device, so
+ * results are deterministic run to run on one device.
  * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, block_size
  * not a power of two >= 16, misaligned pointers, too small a workspace.
  * PKV_EUNSUPPORTED: d not in {64, 128} or H_q/H_kv not in {1, 2, 4, 8}.

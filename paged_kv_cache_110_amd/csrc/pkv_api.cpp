@@ -149,9 +149,8 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
   if (st != PKV_OK) return st;
   if ((int64_t)B * H_kv > INT32_MAX) return PKV_EINVAL;
   const pkv::DecodePlan plan = pkv::decode_plan(B, H_q, H_kv, d, block_size, max_blocks_per_seq);
-  if (plan.num_splits > 65535) return PKV_EINVAL;
-  if (plan.workspace_bytes > 0 &&
-      (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace)))
+  if (plan.num_waves <= 0) return PKV_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
     return PKV_EINVAL;
   return launch_status(pkv::launch_decode(
       static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),

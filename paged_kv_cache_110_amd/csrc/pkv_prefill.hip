@@ -11,9 +11,10 @@
 //  - a workgroup (4 wavefronts) owns one KV head, one sequence and a tile of
 //    query positions; its M dimension packs (query position, head of the
 //    group) pairs, 32 per wavefront, so all G heads share every K/V tile;
-//  - K/V tiles of 64 keys are gathered through the block table (per-row
-//    lookup, so any power-of-two block size works) into LDS, double-buffered,
-//    the next tile's global loads in flight while the current tile computes.
+//  - K/V tiles of 64 keys are gathered through the block table (one look-up
+//    per tile when a tile lies inside one block, per row otherwise, so any
+//    power-of-two block size works) into LDS, double-buffered, the next tile's
+//    global loads all in flight while the current tile computes.
 //    Rows are stored with a 16-byte-chunk XOR swizzle chosen so that both
 //    the K operand reads (one row per lane) and the V transpose reads (four
 //    rows per 16 lanes) hit distinct banks;
@@ -124,32 +125,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int bmask = (1 << bs_log2) - 1;
 
   u32x4 kr[PASSES], vr[PASSES];
+  bool kok[PASSES];
+  // Issue every load of one tile before waiting on any of them: first the
+  // block ids (one scalar load when the tile lies inside one block), then all
+  // K/V rows unconditionally -- rows past the keys this workgroup needs, or
+  // behind an out-of-range block id, read row 0 of block 0 (always valid
+  // memory) and are zeroed when stashed -- so the rows' latencies overlap.
+  const bool tile_in_block = bs_log2 >= 6;  // BN = 64 keys never straddle a block
   auto load_tile = [&](int kt) {
+    int blk[PASSES];
+    if (tile_in_block) {
+      const int b0 = table[(kt * BN) >> bs_log2];  // kt * BN < kend: a valid entry
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) blk[p] = b0;
+    } else {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int j = kt * BN + r0 + RPP * p;
+        blk[p] = j < kend ? table[j >> bs_log2] : 0;
+      }
+    }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int j = kt * BN + r0 + RPP * p;
-      bool ok = j < kend;
-      const int blk = ok ? table[j >> bs_log2] : 0;
-      ok = ok && (unsigned)blk < (unsigned)num_blocks;
-      if (ok) {
-        const int64_t off = (((int64_t)blk << bs_log2) + (j & bmask)) * row_stride;
-        kr[p] = ld16(kbase + off);
-        vr[p] = ld16(vbase + off);
-      } else {
-        kr[p] = u32x4{0, 0, 0, 0};
-        vr[p] = u32x4{0, 0, 0, 0};
-      }
+      kok[p] = j < kend && (unsigned)blk[p] < (unsigned)num_blocks;
+      const int64_t row = kok[p] ? (((int64_t)blk[p] << bs_log2) + (j & bmask)) : 0;
+      kr[p] = ld16(kbase + row * row_stride);
+      vr[p] = ld16(vbase + row * row_stride);
     }
   };
   auto stash_tile = [&](int buf) {
     uint16_t* kt_lds = lds + buf * 2 * TILE;
     uint16_t* vt_lds = kt_lds + TILE;
+    const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int r = r0 + RPP * p;
       const int pc = ch ^ swz<CPR>(r);
-      *reinterpret_cast<u32x4*>(kt_lds + r * D + pc * 8) = kr[p];
-      *reinterpret_cast<u32x4*>(vt_lds + r * D + pc * 8) = vr[p];
+      *reinterpret_cast<u32x4*>(kt_lds + r * D + pc * 8) = kok[p] ? kr[p] : zero;
+      *reinterpret_cast<u32x4*>(vt_lds + r * D + pc * 8) = kok[p] ? vr[p] : zero;
     }
   };
 

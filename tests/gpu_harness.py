@@ -14,6 +14,20 @@ from workloads import Tensors
 TOL = 1e-2  # max-abs error bound for bf16 attention outputs against the float64 oracle
 
 
+def bound(ref: torch.Tensor, tol: float = TOL) -> torch.Tensor:
+    """Per-element error bound: ``tol``, except where a bf16 output cannot meet it.
+
+    Outputs are bf16 (round to nearest even).  Below |o| = 4 the bf16 spacing is
+    at most 2^-6, so rounding costs at most 2^-7 < 1e-2 and the bar is ``tol``.
+    From |o| = 4 up the spacing is 2^-5 or more, and no bf16 value can be within
+    1e-2 of every real; there the bar is half a bf16 spacing of the reference plus
+    2e-3 for the fp32 arithmetic and the bf16 rounding of P before the PV product.
+    """
+    mag = ref.abs().clamp_min(1e-30)
+    half_spacing = torch.exp2(torch.floor(torch.log2(mag)) - 8)
+    return torch.where(mag < 4, torch.full_like(ref, tol), torch.maximum(half_spacing + 2e-3, torch.full_like(ref, tol)))
+
+
 def log(msg: str) -> None:
     print(f"[gpu-test] {msg}", flush=True)
     sys.stdout.flush()
@@ -76,9 +90,13 @@ def assert_close(got: torch.Tensor, ref: torch.Tensor, what: str, tol: float = T
     g = got.detach().float().cpu().double()
     assert torch.isfinite(g).all(), f"{what}: non-finite GPU output"
     assert torch.isfinite(ref).all(), f"{what}: non-finite oracle output"
-    err = (g - ref).abs().max().item() if g.numel() else 0.0
-    log(f"{what}: max abs err {err:.3e} over {g.numel()} values")
-    assert err <= tol, f"{what}: max abs err {err} > {tol}"
+    diff = (g - ref).abs()
+    err = diff.max().item() if g.numel() else 0.0
+    big = int((ref.abs() >= 4).sum())
+    log(f"{what}: max abs err {err:.3e} over {g.numel()} values ({big} with |o| >= 4)")
+    over = diff > bound(ref, tol)
+    assert not over.any(), (f"{what}: {int(over.sum())} values beyond the bound, worst "
+                            f"{diff[over].max().item()} at |o| = {ref[over].abs().max().item()}")
     return err
 
 

@@ -77,10 +77,11 @@ def test_attention_argument_checks_before_launch():
     assert dec(B=0) == 1
     assert dec(d=96) == 2                 # unsupported head size
     assert dec(H_q=48, H_kv=3) == 2       # group of 16
-    # too small a workspace for a split plan
+    # too small a workspace
     ws = lib.pkv_decode_workspace_size(2, 4, 2, 64, 16, 1024)
     assert ws > 0
     assert lib.pkv_decode(p, p, p, p, p, p, 2, 4, 2, 64, 8, 16, 1024, 0.125, p, ws - 1, None) == 1
+    assert lib.pkv_decode(p, p, p, p, p, p, 2, 4, 2, 64, 8, 16, 1024, 0.125, None, ws, None) == 1
 
     def pf(**kw):
         a = {**args, **kw}
@@ -95,14 +96,14 @@ def test_attention_argument_checks_before_launch():
 
 def test_workspace_size_formula():
     lib = _lib.load()
-    # short contexts fit one split: no workspace
-    assert lib.pkv_decode_workspace_size(4, 4, 2, 64, 16, 3) == 0
-    # long contexts: (d + 2) fp32 per query head and split, plus alignment
-    ws = lib.pkv_decode_workspace_size(32, 16, 8, 128, 256, 128)
-    splits = -(-128 * 256 // 512)
-    rows = 32 * 16 * splits
-    assert ws >= rows * (128 + 2) * 4
-    assert ws < rows * (128 + 2) * 4 + 512
+    # two partial slots per resident wavefront, plus 16 bytes per (sequence, KV head)
+    a = lib.pkv_decode_workspace_size(4, 4, 2, 64, 16, 3)
+    b = lib.pkv_decode_workspace_size(5, 4, 2, 64, 16, 3)
+    assert a > 0 and b - a == 2 * 16
+    c = lib.pkv_decode_workspace_size(4, 8, 2, 64, 16, 3)  # G = 4: twice the partial rows
+    assert c > a
+    assert lib.pkv_decode_workspace_size(4, 4, 2, 96, 16, 3) == 0  # unsupported d
+    assert lib.pkv_decode_workspace_size(4, 6, 4, 64, 16, 3) == 0  # H_q % H_kv
 
 
 def _meta_equal(a, b):
