@@ -107,8 +107,16 @@ __global__ __launch_bounds__(64) void decode_kernel(
   // ---- this wavefront's share of the flattened tile list -----------------
   // Units are (sequence, KV head, 16-token tile); sequence b owns
   // H_kv * ceil(len_b / 16) consecutive units, KV heads in order.
+  constexpr int kCachedChunks = 8;  // tile counts of the first 512 sequences stay in registers
+  int cnt[kCachedChunks];
   int64_t part = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
+#pragma unroll
+  for (int c = 0; c < kCachedChunks; ++c) {
+    const int b = c * 64 + lane;
+    cnt[c] = b < B ? (clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile : 0;
+    part += cnt[c];
+  }
+  for (int b0 = kCachedChunks * 64; b0 < B; b0 += 64) {
     const int b = b0 + lane;
     if (b < B) part += (clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile;
   }
@@ -124,10 +132,17 @@ __global__ __launch_bounds__(64) void decode_kernel(
   int64_t sb_base = 0;
   {
     int64_t run = 0;
-    for (int b0 = 0; b0 < B; b0 += 64) {
+    for (int b0 = 0, c = 0; b0 < B; b0 += 64, ++c) {
       const int b = b0 + lane;
-      const int64_t n =
-          b < B ? (int64_t)((clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile) * H_kv : 0;
+      int nt = 0;
+      if (c < kCachedChunks) {
+#pragma unroll
+        for (int k = 0; k < kCachedChunks; ++k)
+          if (k == c) nt = cnt[k];
+      } else if (b < B) {
+        nt = (clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile;
+      }
+      const int64_t n = (int64_t)nt * H_kv;
       const int64_t incl = wave_incl_scan_i64(n, lane) + run;
       const int64_t excl = incl - n;
       const unsigned long long hit = __ballot(n > 0 && excl <= start && start < incl);
@@ -177,11 +192,36 @@ __global__ __launch_bounds__(64) void decode_kernel(
   Cursor C = L;                   // compute cursor
   int64_t lstep = 0;
 
+  // q of the next segment is loaded by the load cursor when it enters that
+  // segment, so starting the segment does not drain the tile ring.  One
+  // buffer: if it is still taken when another segment starts (segments of
+  // fewer than NBUF - 1 tiles), that segment loads its q when it starts.
+  uint32_t qn[G][EPL / 2];
+  int64_t qn_seg = -1;  // flattened (sequence, KV head) index held in qn, -1 = free
+  auto load_q = [&](int b, int h, uint32_t (&dst)[G][EPL / 2]) {
+    const int64_t head0 = (int64_t)b * H_q + (int64_t)h * G;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const u32x4 v = ld16(q + (head0 + g) * D + dofs(w));
+        dst[g][4 * w + 0] = v[0];
+        dst[g][4 * w + 1] = v[1];
+        dst[g][4 * w + 2] = v[2];
+        dst[g][4 * w + 3] = v[3];
+      }
+    }
+  };
+
   // Loads the tile under the load cursor, then moves the cursor on (while it
   // has tiles left; past the end it stays on the last tile, whose re-read is
   // an L2 hit, and the tile is marked empty).
   auto load_tile = [&](u32x4 (&kx)[TPL][NW], u32x4 (&vx)[TPL][NW], bool (&ok)[TPL]) {
     const bool real = lstep < R;
+    if (real && lstep > 0 && L.j == 0 && qn_seg < 0) {
+      load_q(L.b, L.h, qn);
+      qn_seg = (int64_t)L.b * H_kv + L.h;
+    }
     const int t = L.j * kDecodeTile;
     int blk = block_tables[(int64_t)L.b * maxb + (t >> bs_log2)];
     const bool blk_ok = real && (unsigned)blk < (unsigned)num_blocks;
@@ -210,17 +250,17 @@ __global__ __launch_bounds__(64) void decode_kernel(
   float m[G], l[G];
 
   auto begin_segment = [&]() {
-    const int64_t head0 = (int64_t)C.b * H_q + (int64_t)C.h * G;
+    if (qn_seg == (int64_t)C.b * H_kv + C.h) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < EPL / 2; ++k) qw[g][k] = qn[g][k];
+      qn_seg = -1;
+    } else {
+      load_q(C.b, C.h, qw);
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const u32x4 v = ld16(q + (head0 + g) * D + dofs(w));
-        qw[g][4 * w + 0] = v[0];
-        qw[g][4 * w + 1] = v[1];
-        qw[g][4 * w + 2] = v[2];
-        qw[g][4 * w + 3] = v[3];
-      }
       m[g] = kNegSentinel;
       l[g] = 0.f;
 #pragma unroll
