@@ -56,6 +56,25 @@ def prefill_flops(plan) -> int:
     return 4 * plan.d * plan.H_q * pairs
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed PMC record, or None when the
+    decode kernel's source has changed since the counters were taken."""
+    import hashlib
+
+    rec_path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(rec_path):
+        return None
+    rec = json.load(open(rec_path)).get(workload)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in ("pkv_decode.hip", "device_common.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_110_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != rec["decode_source_sha256"]:
+        return None
+    return (rec["fetch_mb_per_call"] + rec["write_mb_per_call"]) * 1e6
+
+
 # ------------------------------------------------------------------- timing
 
 class Timer:
@@ -288,9 +307,12 @@ def main() -> int:
         unit = "GB/s"
         per_launch = decode_bytes(plan)
         achieved = per_launch / (main_res["attn_ms"] * 1e-3) / 1e9
-        roofline = dict(bound="hbm", kernel="pkv_decode (decode_split_kernel + decode_merge_kernel)",
+        traffic = measured_traffic(plan.name)
+        roofline = dict(bound="hbm", kernel="pkv_decode call (decode_kernel + decode_merge_kernel)",
                         achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        frac=round(achieved / HBM_PEAK_GBS, 4),
+                        traffic=None if traffic is None else round(traffic),
+                        traffic_unit="bytes per call (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
                         bytes_per_launch=per_launch, avg_launch_ms=round(main_res["attn_ms"], 4))
     else:
         value = s["prefill_tflops"]
