@@ -41,13 +41,16 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
       (__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// 16-byte chunk swizzle: rows r..r+7 map one logical chunk to 8 distinct
-// chunks, and rows 4k..4k+3 map a pair of adjacent chunks to 8 distinct chunks.
+// 16-byte chunk swizzle of the K/V tiles in LDS (a row is d bf16 = CPR chunks).
+// gfx950 serves 16 lanes of 16-byte reads and 32 lanes of 8-byte reads per LDS
+// cycle over 64 four-byte banks.  With these XOR patterns (checked with the
+// SQ_LDS_BANK_CONFLICT counter) neither the K operand reads (one row per lane,
+// 16 consecutive rows on one chunk) nor the V transpose reads (4 consecutive
+// rows x 4 chunks per 32 lanes) nor the tile stores conflict.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-  int g = ((row & 3) << 1) | ((row >> 2) & 1);
-  if constexpr (CPR >= 16) g |= (row & 8);
-  return g;
+  if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 template <int D, int G>
@@ -115,101 +118,127 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   float m = kNegSentinel;
   float l = 0.f;
 
-  // cooperative tile loader: thread -> (chunk, rows)
+  // ---- per-lane offsets, computed once -------------------------------------
+  // cooperative tile loader: thread -> (chunk ch, rows r0 + RPP * p)
   const int ch = tid % CPR;
   const int r0 = tid / CPR;
-  const int64_t row_stride = (int64_t)H_kv * D;
-  const uint16_t* kbase = k_cache + (int64_t)h_kv * D + ch * 8;
-  const uint16_t* vbase = v_cache + (int64_t)h_kv * D + ch * 8;
+  const int row_stride = H_kv * D;  // elements between token rows of the cache
+  const int goff = r0 * row_stride + ch * 8;  // element offset of this thread's first row
+  // the LDS slot of this thread's chunk; rows r0 + RPP * p share their low four bits
+  const int soff = r0 * D + ((ch ^ swz<CPR>(r0)) << 3);
+  // K operand reads: row kb * 32 + mrow, logical chunk 2 * ks + half.  The row
+  // base is a multiple of the row size, so the swizzled chunk is one XOR away:
+  // element offset = kbase_lane ^ (16 * ks).
+  const int kbase_lane = mrow * D + ((half ^ swz<CPR>(mrow)) << 3);
+  // V^T operand reads: rows kb * 32 + 16 * s2 + rlo (+ 8), 4 columns at col
+  const int i16 = lane & 15;
+  const int grp16 = lane >> 4;
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int col = db * 32 + 16 * (grp16 & 1) + 4 * (i16 & 3);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int rlo = 4 * half + (i16 >> 2) + 8 * hi;
+      voff[db][hi] = rlo * D + (((col >> 3) ^ swz<CPR>(rlo)) << 3) + (col & 7);
+    }
+  }
+  const uint16_t* khead = k_cache + (int64_t)h_kv * D;
+  const uint16_t* vhead = v_cache + (int64_t)h_kv * D;
   const int32_t* table = block_tables + (int64_t)b * maxb;
   const int bmask = (1 << bs_log2) - 1;
 
   u32x4 kr[PASSES], vr[PASSES];
   bool kok[PASSES];
-  // Issue every load of one tile before waiting on any of them: first the
-  // block ids (one scalar load when the tile lies inside one block), then all
-  // K/V rows unconditionally -- rows past the keys this workgroup needs, or
-  // behind an out-of-range block id, read row 0 of block 0 (always valid
-  // memory) and are zeroed when stashed -- so the rows' latencies overlap.
-  const bool tile_in_block = bs_log2 >= 6;  // BN = 64 keys never straddle a block
+  bool full_next = true;  // the tile in kr/vr needs no zeroing
+  // Issues every global load of tile kt before any wait.  When a tile lies
+  // inside one block (block size >= 64) its base is one scalar look-up and the
+  // rows are fixed offsets from it; otherwise each row is looked up (all
+  // look-ups first).  Rows past the keys this workgroup needs, or behind an
+  // out-of-range block id, read valid memory and are zeroed when stashed.
+  const bool tile_in_block = bs_log2 >= 6;
   auto load_tile = [&](int kt) {
-    int blk[PASSES];
     if (tile_in_block) {
-      const int b0 = table[(kt * BN) >> bs_log2];  // kt * BN < kend: a valid entry
+      int blk = table[(kt * BN) >> bs_log2];  // kt * BN < kend: a valid entry
+      const bool blk_ok = (unsigned)blk < (unsigned)num_blocks;
+      blk = blk_ok ? blk : 0;
+      const int64_t base = (((int64_t)blk << bs_log2) + ((kt * BN) & bmask)) * row_stride;
+      const uint16_t* kb = khead + base;
+      const uint16_t* vb = vhead + base;
 #pragma unroll
-      for (int p = 0; p < PASSES; ++p) blk[p] = b0;
+      for (int p = 0; p < PASSES; ++p) {
+        kok[p] = blk_ok && kt * BN + r0 + RPP * p < kend;
+        kr[p] = ld16(kb + (int64_t)RPP * p * row_stride + goff);
+        vr[p] = ld16(vb + (int64_t)RPP * p * row_stride + goff);
+      }
+      full_next = blk_ok && kt * BN + BN <= kend;
     } else {
+      int blk[PASSES];
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         const int j = kt * BN + r0 + RPP * p;
         blk[p] = j < kend ? table[j >> bs_log2] : 0;
       }
-    }
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int j = kt * BN + r0 + RPP * p;
-      kok[p] = j < kend && (unsigned)blk[p] < (unsigned)num_blocks;
-      const int64_t row = kok[p] ? (((int64_t)blk[p] << bs_log2) + (j & bmask)) : 0;
-      kr[p] = ld16(kbase + row * row_stride);
-      vr[p] = ld16(vbase + row * row_stride);
+      for (int p = 0; p < PASSES; ++p) {
+        const int j = kt * BN + r0 + RPP * p;
+        kok[p] = j < kend && (unsigned)blk[p] < (unsigned)num_blocks;
+        const int64_t row = kok[p] ? (((int64_t)blk[p] << bs_log2) + (j & bmask)) : 0;
+        kr[p] = ld16(khead + row * row_stride + ch * 8);
+        vr[p] = ld16(vhead + row * row_stride + ch * 8);
+      }
+      full_next = false;
     }
   };
-  auto stash_tile = [&](int buf) {
-    uint16_t* kt_lds = lds + buf * 2 * TILE;
+  auto stash_tile = [&](uint16_t* kt_lds) {
     uint16_t* vt_lds = kt_lds + TILE;
-    const u32x4 zero = {0, 0, 0, 0};
+    if (full_next) {
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int r = r0 + RPP * p;
-      const int pc = ch ^ swz<CPR>(r);
-      *reinterpret_cast<u32x4*>(kt_lds + r * D + pc * 8) = kok[p] ? kr[p] : zero;
-      *reinterpret_cast<u32x4*>(vt_lds + r * D + pc * 8) = kok[p] ? vr[p] : zero;
+      for (int p = 0; p < PASSES; ++p) {
+        *reinterpret_cast<u32x4*>(kt_lds + soff + RPP * p * D) = kr[p];
+        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = vr[p];
+      }
+    } else {
+      const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        *reinterpret_cast<u32x4*>(kt_lds + soff + RPP * p * D) = kok[p] ? kr[p] : zero;
+        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = kok[p] ? vr[p] : zero;
+      }
     }
   };
 
-  load_tile(0);
-  stash_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) load_tile(kt + 1);
-    const uint16_t* kt_lds = lds + buf * 2 * TILE;
+  // One 64-key tile from LDS buffer BUF: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto compute_tile = [&](int kt, const uint16_t* kt_lds) {
     const uint16_t* vt_lds = kt_lds + TILE;
-
-    // S^T for two 32-key blocks
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
-      const int row = kb * 32 + mrow;
-      const int sw = swz<CPR>(row);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int pc = (2 * ks + half) ^ sw;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + row * D + pc * 8);
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(kt_lds + (kbase_lane ^ (16 * ks)) + kb * 32 * D);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks],
                                                            sacc[kb], 0, 0, 0);
       }
     }
-
-    // scale, causal mask on diagonal tiles, tile max of this row
-    const bool need_mask = kt * BN + BN - 1 > wave_first_pos;
+    // causal mask, only on tiles that reach past this wavefront's first position
+    if (kt * BN + BN - 1 > wave_first_pos) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > qpos) sacc[kb][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = sacc[kb][r] * scale_log2e;
-        if (need_mask) {
-          const int key = kt * BN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          sv = key > qpos ? -INFINITY : sv;
-        }
-        sacc[kb][r] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx *= scale_log2e;  // the scale is positive: max commutes with it
     mx = fmaxf(mx, shfl_xor_f32(mx, 32));
     if (__any(mx > m + kPrefillLazy)) {
       const float mn = fmaxf(m, mx);
@@ -219,48 +248,44 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
-
-    // P (bf16) in the B-operand layout of O^T += V^T P^T
+    // P = 2^(s * scale * log2 e - m), rounded to bf16 for the PV product
     bf16x8 pf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = fast_exp2(sacc[kb][8 * s2 + e] - m);
+          const float p = fast_exp2(__builtin_fmaf(sacc[kb][8 * s2 + e], scale_log2e, -m));
           l += p;
           pf[kb][s2][e] = (__bf16)p;
         }
-      }
-    }
-
-    // O^T += V^T P^T, V^T operands by transpose reads of the row-major V tile
-    const int i16 = lane & 15;
-    const int grp16 = lane >> 4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int col = db * 32 + 16 * (grp16 & 1) + 4 * (i16 & 3);
-      const int chunk = col >> 3;
-      const int sub8 = col & 7;  // 0 or 4 elements into the chunk
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int k0 = kb * 32 + 16 * s2 + 4 * half;
-          const int ra = k0 + (i16 >> 2);
-          const int rb = ra + 8;
-          const i16x4 va = lds_read_tr16(vt_lds + ra * D + ((chunk ^ swz<CPR>(ra)) << 3) + sub8);
-          const i16x4 vb = lds_read_tr16(vt_lds + rb * D + ((chunk ^ swz<CPR>(rb)) << 3) + sub8);
+          const int rofs = (kb * 32 + 16 * s2) * D;
+          const i16x4 va = lds_read_tr16(vt_lds + voff[db][0] + rofs);
+          const i16x4 vb = lds_read_tr16(vt_lds + voff[db][1] + rofs);
           typedef short i16x8 __attribute__((ext_vector_type(8)));
           const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf[kb][s2],
-                                                          o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
+                                                          pf[kb][s2], o[db], 0, 0, 0);
         }
-      }
-    }
+  };
 
-    if (more) stash_tile(buf ^ 1);
+  load_tile(0);
+  stash_tile(lds);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    uint16_t* cur = lds + (kt & 1) * 2 * TILE;
+    uint16_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
+    const bool more = kt + 1 < ntiles;
+    if (more) load_tile(kt + 1);
+    compute_tile(kt, cur);
+    if (more) stash_tile(nxt);
     __syncthreads();
   }
 
