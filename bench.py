@@ -121,7 +121,7 @@ def run_workload(name, steps, warmup, pools, torch, pkv, log):
     if plan.kind == "decode":
         nbytes = pkv.decode_workspace_size(plan.B, plan.H_q, plan.H_kv, plan.d, plan.block_size,
                                            plan.max_blocks_per_seq)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
         outs = [torch.empty_like(t.q[0]) for t in tens]
     torch.cuda.synchronize()
     log(f"{name}: inputs ready in {time.time() - t0:.1f}s ({plan.B} seqs, {plan.num_blocks} blocks,"

@@ -119,9 +119,11 @@ pkv_status pkv_store(const void* key, int64_t key_stride, const void* value,
 /*
  * Bytes of device workspace pkv_decode needs for these sizes on the current
  * HIP device: two fp32 partial results (max, sum, d-vector) per query head of
- * a group for every resident wavefront of the device, plus a 16-byte record
- * per (sequence, KV head).  Query it with the device current that will run
- * the decode.  0 for invalid or unsupported sizes.
+ * a group for every share of the work schedule (8 shares per resident
+ * wavefront of the device), a 16-byte record per (sequence, KV head), and a
+ * 256-byte line holding the schedule's share counter.  Query it with the
+ * device current that will run the decode.  0 for invalid or unsupported
+ * sizes.
  */
 size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d,
                                  int32_t block_size, int32_t max_blocks_per_seq);
@@ -139,17 +141,23 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d
  *                 zero output row; values above max_blocks_per_seq*block_size
  *                 are clamped to it
  *   workspace     device, >= pkv_decode_workspace_size(...) bytes, 16-byte
- *                 aligned; contents on entry are irrelevant and unspecified on
- *                 return
+ *                 aligned, zero-filled before its first use (e.g. hipMemset).
+ *                 Each call leaves it ready for the next one; calls that share
+ *                 a workspace must run in stream order, never concurrently.
+ *                 After a PKV_ELAUNCH it must be zero-filled again.
  * The causal mask of the pages' call is a no-op for one query per sequence.
- * The work (every 16-token tile of every (sequence, KV head)) is split evenly
- * over one wavefront per resident slot of the device; pieces of a sequence
- * that straddle wavefronts are merged with a log-sum-exp rescale in a second
- * kernel.  The split depends only on the context lengths and the device, so
- * results are deterministic run to run on one device.
+ * The work (every 16-token tile of every (sequence, KV head)) is cut into
+ * shares: one static share per resident wavefront of the device (about three
+ * quarters of the work), then shrinking shares that wavefronts take from an
+ * atomic counter as they finish, so all of them stop at nearly the same time.
+ * Pieces of a sequence that span shares are merged with a log-sum-exp rescale
+ * in a second kernel, in share order, so the result does not depend on which
+ * wavefront took which share: results are deterministic run to run on one
+ * device.
  * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, block_size
  * not a power of two >= 16, misaligned pointers, too small a workspace.
- * PKV_EUNSUPPORTED: d not in {64, 128} or H_q/H_kv not in {1, 2, 4, 8}.
+ * PKV_EUNSUPPORTED: d not in {64, 128}; H_q/H_kv not in {1, 2, 4, 8};
+ * B * H_kv * ceil(max_blocks_per_seq * block_size / 16) > INT32_MAX.
  */
 pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens, int32_t B,

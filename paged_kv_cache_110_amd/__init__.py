@@ -143,7 +143,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
     ws_bytes = decode_workspace_size(B, H_q, H_kv, d, bs, maxb)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
     have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     check("pkv_decode", load().pkv_decode(

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = ["pkv_api.cpp", "pkv_store.hip", "pkv_decode.hip", "pkv_prefill.hip"]
-HEADERS = ["device_common.h", "pkv_internal.h"]
+HEADERS = ["decode_schedule.h", "device_common.h", "pkv_internal.h"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -24,6 +24,9 @@ FLAGS = [
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # keep single-lane atomics as written: the wave-level atomic rewrite reads
+    # the result back at once, which stalls on every load still in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

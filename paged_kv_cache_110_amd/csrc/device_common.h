@@ -60,6 +60,28 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
   return __shfl_xor(x, mask, 64);
 }
 
+constexpr int kDppRowRor8 = 0x128;  // lane i <- lane i ^ 8 within a row of 16
+
+// Sum / max over the lanes l, l ^ S, l ^ 2S, ... (S in {8, 16, 32}): lanes
+// that share l % S.  Every lane ends with the result.  The exchanges run on
+// the vector ALU (DPP row rotate by 8, v_permlane16_swap, v_permlane32_swap:
+// each swap of x with itself yields the two halves of every lane pair, so
+// combining its two outputs gives the pair's sum or max in all lanes).
+template <int S, bool MAX>
+__device__ __forceinline__ float cross_reduce(float x) {
+  static_assert(S == 8 || S == 16 || S == 32, "stride");
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (S <= 8) x = op(x, dpp_f32<kDppRowRor8>(x));
+  if constexpr (S <= 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // 16-byte global load / store helpers (addresses must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

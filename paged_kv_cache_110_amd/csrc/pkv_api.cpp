@@ -19,6 +19,13 @@ bool supported_group(int32_t H_q, int32_t H_kv) {
   return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
+// The decode schedule counts (sequence, KV head, 16-token tile) units in
+// int32: the most a table of this width can describe must fit.
+bool decode_units_fit(int32_t B, int32_t H_kv, int32_t block_size, int32_t max_blocks_per_seq) {
+  const int64_t tiles = ((int64_t)max_blocks_per_seq * block_size + 15) / 16;
+  return (int64_t)B * H_kv * tiles <= INT32_MAX;
+}
+
 pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
 
 // Checks shared by the two attention calls.
@@ -135,6 +142,7 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d
       !pow2_ge16(block_size) || H_q % H_kv != 0)
     return 0;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX) return 0;
+  if (!decode_units_fit(B, H_kv, block_size, max_blocks_per_seq)) return 0;
   return pkv::decode_plan(B, H_q, H_kv, d, block_size, max_blocks_per_seq).workspace_bytes;
 }
 
@@ -148,6 +156,7 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
                                   num_blocks, block_size, max_blocks_per_seq);
   if (st != PKV_OK) return st;
   if ((int64_t)B * H_kv > INT32_MAX) return PKV_EINVAL;
+  if (!decode_units_fit(B, H_kv, block_size, max_blocks_per_seq)) return PKV_EUNSUPPORTED;
   const pkv::DecodePlan plan = pkv::decode_plan(B, H_q, H_kv, d, block_size, max_blocks_per_seq);
   if (plan.num_waves <= 0) return PKV_EUNSUPPORTED;
   if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))

@@ -40,6 +40,7 @@
 //    wavefront's two partial slots, and decode_merge_kernel combines them.
 #include <stdlib.h>
 
+#include "decode_schedule.h"
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -47,46 +48,46 @@ namespace pkv {
 
 constexpr int kDecodeTile = 16;       // tokens per tile; divides every supported block size
 constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is updated
-constexpr int kMinTilesPerWave = 32;  // a wavefront streams at least 512 tokens of one head
+constexpr int kSeqCache = 512;        // sequences whose unit offsets are kept in LDS
 
-// Where the partials of one (sequence, KV head) segment live: the wavefronts
-// w_first .. w_first + nparts - 1 hold one piece each, in partial slot
-// `slot_first` for the first of them and slot 0 for the others.
+// Where the partial results of one (sequence, KV head) segment live: it was
+// cut into the shares k_first .. k_last, one piece each (k_first == k_last:
+// one piece, written directly).
 struct SegInfo {
-  int32_t nparts;
-  int32_t w_first;
-  int32_t slot_first;
-  int32_t pad;
+  int32_t k_first;
+  int32_t k_last;
+  int32_t pad0, pad1;
 };
 
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
-__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t x, int lane) {
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int64_t y = __shfl_up(x, off, 64);
+    const int y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
   return x;
 }
 
-template <int D, int G, int EPL, int NBUF>
-__global__ __launch_bounds__(64) void decode_kernel(
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Unit counts fit in int32: the host rejects shapes where
+// B * H_kv * ceil(max_blocks_per_seq * block_size / 16) could exceed INT32_MAX.
+template <int D, int G, int EPL, int NBUF, int WPE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, SegInfo* __restrict__ ws_seg,
-    int32_t B, int32_t H_kv, int32_t num_blocks, int32_t bs_log2, int32_t maxb,
-    float scale_log2e) {
+    int32_t* __restrict__ queue, int32_t B, int32_t H_kv, int32_t num_blocks, int32_t bs_log2,
+    int32_t maxb, float scale_log2e) {
   constexpr int LPT = D / EPL;           // lanes per token
   constexpr int TPI = 64 / LPT;          // tokens side by side in a wave
   constexpr int TPL = kDecodeTile / TPI; // tokens per lane per tile
   constexpr int NW = EPL / 8;            // 128-bit words per lane per row
   static_assert(TPI * TPL == kDecodeTile, "tile shape");
+
+  __shared__ int pre[kSeqCache + 1];  // units of the sequences before b
+  __shared__ int lenc[kSeqCache];     // clamped context length of b
 
   const int lane = threadIdx.x;
   const int grp = lane / LPT;
@@ -99,105 +100,182 @@ __global__ __launch_bounds__(64) void decode_kernel(
   const int cap = maxb << bs_log2;
   const int bmask = (1 << bs_log2) - 1;
   const int rs = H_kv * D;  // elements between consecutive token rows
-  const int64_t W = gridDim.x;
-  const int64_t wv = blockIdx.x;
+  const int W = gridDim.x;
+  const int wv = blockIdx.x;
 
   auto clamp_len = [&](int len) { return len < 0 ? 0 : (len > cap ? cap : len); };
+  auto tiles_of = [&](int len) { return (clamp_len(len) + kDecodeTile - 1) / kDecodeTile; };
 
-  // ---- this wavefront's share of the flattened tile list -----------------
+  // ---- unit offsets of the sequences -----------------------------------
   // Units are (sequence, KV head, 16-token tile); sequence b owns
   // H_kv * ceil(len_b / 16) consecutive units, KV heads in order.
-  constexpr int kCachedChunks = 8;  // tile counts of the first 512 sequences stay in registers
-  int cnt[kCachedChunks];
-  int64_t part = 0;
-#pragma unroll
-  for (int c = 0; c < kCachedChunks; ++c) {
-    const int b = c * 64 + lane;
-    cnt[c] = b < B ? (clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile : 0;
-    part += cnt[c];
-  }
-  for (int b0 = kCachedChunks * 64; b0 < B; b0 += 64) {
-    const int b = b0 + lane;
-    if (b < B) part += (clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile;
-  }
-  const int64_t total = wave_sum_i64(part) * H_kv;
-  int64_t U = (total + W - 1) / W;
-  U = U < kMinTilesPerWave ? kMinTilesPerWave : U;
-  const int64_t start = wv * U;
-  if (start >= total) return;
-  const int64_t end = start + U < total ? start + U : total;
-
-  // sequence holding `start`, and the units before it
-  int sb = 0;
-  int64_t sb_base = 0;
+  const int nb_cached = B < kSeqCache ? B : kSeqCache;
+  int T = 0;
   {
-    int64_t run = 0;
-    for (int b0 = 0, c = 0; b0 < B; b0 += 64, ++c) {
-      const int b = b0 + lane;
-      int nt = 0;
-      if (c < kCachedChunks) {
+    constexpr int kChunks = kSeqCache / 64;
+    int cnt[kChunks];
 #pragma unroll
-        for (int k = 0; k < kCachedChunks; ++k)
-          if (k == c) nt = cnt[k];
-      } else if (b < B) {
-        nt = (clamp_len(context_lens[b]) + kDecodeTile - 1) / kDecodeTile;
-      }
-      const int64_t n = (int64_t)nt * H_kv;
-      const int64_t incl = wave_incl_scan_i64(n, lane) + run;
-      const int64_t excl = incl - n;
-      const unsigned long long hit = __ballot(n > 0 && excl <= start && start < incl);
-      if (hit) {
-        const int idx = __ffsll((long long)hit) - 1;
-        sb = b0 + idx;
-        sb_base = __shfl(excl, idx, 64);
-        break;
-      }
-      run = __shfl(incl, 63, 64);
+    for (int c = 0; c < kChunks; ++c) {
+      const int b = c * 64 + lane;
+      const int len = b < B ? clamp_len(context_lens[b]) : 0;
+      lenc[c * 64 + lane] = len;
+      cnt[c] = (len + kDecodeTile - 1) / kDecodeTile;
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int n = cnt[c] * H_kv;
+      const int incl = wave_incl_scan(n, lane) + T;
+      pre[c * 64 + lane] = incl - n;
+      T = uniform(__shfl(incl, 63, 64));
+    }
+    if (lane == 0) pre[kSeqCache] = T;
+    for (int b0 = kSeqCache; b0 < B; b0 += 64) {
+      const int b = b0 + lane;
+      const int n = b < B ? tiles_of(context_lens[b]) * H_kv : 0;
+      T += uniform(__shfl(wave_incl_scan(n, lane), 63, 64));
     }
   }
 
-  // A cursor walks the units in order: sequence b (length len, nt tiles),
-  // KV head h, tile j; base = units before sequence b.  All wave-uniform.
+  __syncthreads();
+  // pre[] is read back with relaxed atomic loads: they stay LDS reads and are
+  // not hoisted into registers that would stay live across the tile loop.
+  auto pre_at = [&](int i) {
+    return __hip_atomic_load(&pre[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  // clamped length of sequence b (from LDS for the first kSeqCache sequences)
+  auto len_of = [&](int b) {
+    return b < kSeqCache
+               ? uniform(__hip_atomic_load(&lenc[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+               : clamp_len(context_lens[b]);
+  };
+  const int T_cached = uniform(pre_at(nb_cached));
+
+  // ---- share layout (see decode_schedule.h) ---------------------------------
+  // Divisions run on the vector ALU: pin every result that addresses memory
+  // to scalar registers, so block-table reads stay scalar loads instead of
+  // vector loads whose wait would drain the tile ring.
+  ShareSchedule sch = ShareSchedule::make(T, W);
+  sch.S0 = uniform(sch.S0);
+  sch.P1 = uniform(sch.P1);
+  sch.S1 = uniform(sch.S1);
+  const bool dynamic = sch.dynamic();
+  const int num_shares = sch.num_shares();
+
+  // A cursor walks units in order: sequence b (length len, nt tiles), KV head
+  // h, tile j; base = units before sequence b; u = the unit; [us, ue) = the
+  // share being walked, k its index.  All wave-uniform.
   struct Cursor {
-    int b, h, j, nt, len;
-    int64_t base;
+    int b, h, j, nt, len, base, u, us, ue, k;
   };
-  auto make_cursor = [&]() {
-    Cursor c;
-    c.b = sb;
-    c.len = clamp_len(context_lens[sb]);
+  // Position a cursor on unit u (< T): the last sequence whose offset is <= u.
+  auto locate = [&](Cursor& c, int u) {
+    int b = 0, base = 0;
+    if (u < T_cached) {
+      constexpr int kStride = kSeqCache / 64;
+      const int i0 = lane * kStride;
+      const bool hit0 = i0 < nb_cached && pre_at(i0 < nb_cached ? i0 : 0) <= u;
+      const int c0 = 63 - __clzll(__ballot(hit0));
+      const int i1 = c0 * kStride + lane;
+      const bool hit1 = lane < kStride && i1 < nb_cached && pre_at(i1 < nb_cached ? i1 : 0) <= u;
+      b = c0 * kStride + (63 - __clzll(__ballot(hit1)));
+      base = uniform(pre_at(b));
+    } else {
+      int run = T_cached;
+      for (int b0 = kSeqCache; b0 < B; b0 += 64) {
+        const int bb = b0 + lane;
+        const int n = bb < B ? tiles_of(context_lens[bb]) * H_kv : 0;
+        const int incl = wave_incl_scan(n, lane) + run;
+        const int excl = incl - n;
+        const unsigned long long hit = __ballot(n > 0 && excl <= u && u < incl);
+        if (hit) {
+          const int idx = __ffsll((long long)hit) - 1;
+          b = b0 + idx;
+          base = uniform(__shfl(excl, idx, 64));
+          break;
+        }
+        run = uniform(__shfl(incl, 63, 64));
+      }
+    }
+    c.b = uniform(b);
+    c.len = len_of(c.b);
     c.nt = (c.len + kDecodeTile - 1) / kDecodeTile;
-    c.base = sb_base;
-    const int64_t off = start - sb_base;
-    c.h = (int)(off / c.nt);
-    c.j = (int)(off - (int64_t)c.h * c.nt);
-    return c;
+    c.base = base;
+    const int off = u - base;
+    c.h = uniform(off / c.nt);
+    c.j = off - c.h * c.nt;
+    c.u = u;
   };
-  auto advance = [&](Cursor& c) {
+  auto pin = [&](Cursor& c) {  // keep the cursor in scalar registers
+    c.b = uniform(c.b);
+    c.h = uniform(c.h);
+    c.j = uniform(c.j);
+    c.nt = uniform(c.nt);
+    c.len = uniform(c.len);
+    c.base = uniform(c.base);
+    c.u = uniform(c.u);
+    c.us = uniform(c.us);
+    c.ue = uniform(c.ue);
+    c.k = uniform(c.k);
+  };
+  auto step_unit = [&](Cursor& c) {  // next unit inside the share
+    ++c.u;
     if (++c.j < c.nt) return;
     c.j = 0;
     if (++c.h < H_kv) return;
     c.h = 0;
-    c.base += (int64_t)c.nt * H_kv;
+    c.base += c.nt * H_kv;
     do {  // skip empty sequences; never runs past the last unit of the call
       ++c.b;
-      c.len = clamp_len(context_lens[c.b]);
+      c.len = len_of(c.b);
       c.nt = (c.len + kDecodeTile - 1) / kDecodeTile;
     } while (c.nt == 0 && c.b + 1 < B);
   };
 
-  // ---- the tile ring -------------------------------------------------------
-  const int64_t R = end - start;  // tiles this wavefront computes
-  Cursor L = make_cursor();       // load cursor, NBUF - 1 tiles ahead
-  Cursor C = L;                   // compute cursor
-  int64_t lstep = 0;
+  // The next dynamic share is requested in the step that loads the second-to-
+  // last tile of the current one, before that step's tile loads, and read
+  // after the computation of the following step: by then every load issued
+  // before the request has been waited for anyway, so reading the counter
+  // costs no extra wait.
+  // Lane 0 of grab[i]: value the counter returned for a request made while
+  // loading ring slot i (one register per slot, so the read one step later is
+  // known not to race a request of its own step).
+  int grab[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) grab[i] = 0;
+  bool switch_pending = false;
 
-  // q of the next segment is loaded by the load cursor when it enters that
-  // segment, so starting the segment does not drain the tile ring.  One
-  // buffer: if it is still taken when another segment starts (segments of
-  // fewer than NBUF - 1 tiles), that segment loads its q when it starts.
-  uint32_t qn[G][EPL / 2];
-  int64_t qn_seg = -1;  // flattened (sequence, KV head) index held in qn, -1 = free
+  Cursor L;  // load cursor, NBUF - 1 tiles ahead of the computation
+  sch.range(wv, L.us, L.ue);
+  L.us = uniform(L.us);
+  L.ue = uniform(L.ue);
+  if (L.us >= T) return;
+  bool l_active = true;
+  L.k = wv;
+  locate(L, L.us);
+  pin(L);
+
+  // Per ring slot: what the tile is, for the compute side (wave-uniform).
+  // A piece is the part of one (sequence, KV head) segment inside one share.
+  enum : int {
+    kValid = 1,        // a real tile
+    kBegin = 2,        // first tile of a piece
+    kEnd = 4,          // last tile of a piece
+    kBeganBefore = 8,  // the piece's segment started in an earlier share
+    kSegEnd = 16,      // the piece holds the segment's last tile
+    kLast = 32         // the wavefront's last tile
+  };
+  struct Meta {
+    int b, h, flags, k;
+    int rows;  // valid key rows of the tile (0 for an empty tile)
+  };
+
+  // q of the next pieces is loaded by the load cursor when it reaches their
+  // first tiles, so starting a piece does not drain the tile ring.  Two
+  // buffers cover the NBUF - 1 tiles between the cursors even for one-tile
+  // pieces; if both are taken the piece loads its q when it starts.
+  constexpr int kQBufs = NBUF > 2 ? 2 : 1;
+  uint32_t qn0[G][EPL / 2], qn1[G][EPL / 2];
+  int qn_seg0 = -1, qn_seg1 = -1;  // (sequence, KV head) index held, -1 = free
   auto load_q = [&](int b, int h, uint32_t (&dst)[G][EPL / 2]) {
     const int64_t head0 = (int64_t)b * H_q + (int64_t)h * G;
 #pragma unroll
@@ -213,14 +291,36 @@ __global__ __launch_bounds__(64) void decode_kernel(
     }
   };
 
-  // Loads the tile under the load cursor, then moves the cursor on (while it
-  // has tiles left; past the end it stays on the last tile, whose re-read is
-  // an L2 hit, and the tile is marked empty).
-  auto load_tile = [&](u32x4 (&kx)[TPL][NW], u32x4 (&vx)[TPL][NW], bool (&ok)[TPL]) {
-    const bool real = lstep < R;
-    if (real && lstep > 0 && L.j == 0 && qn_seg < 0) {
-      load_q(L.b, L.h, qn);
-      qn_seg = (int64_t)L.b * H_kv + L.h;
+  // Loads the tile under the load cursor and moves the cursor on.  Once the
+  // wavefront has no work left the cursor stays on its last tile, whose
+  // re-read is an L2 hit, and the tile is marked empty.
+  auto load_tile = [&](u32x4 (&kx)[TPL][NW], u32x4 (&vx)[TPL][NW], Meta& mt, int& grab_slot) {
+    pin(L);
+    const bool real = uniform(l_active ? 1 : 0) != 0;
+    mt.flags = 0;
+    // Ask for the next share when loading the current one's second-to-last
+    // tile (its only tile for one-tile shares); switch after the last.
+    // (A one-tile share has no earlier tile: it asks when it ends.)
+    if (real && L.u + 2 == L.ue && dynamic && lane == 0) grab_slot = atomicAdd(queue, 1);
+    if (real && L.u + 1 == L.ue) switch_pending = true;
+    if (real) {
+      const bool begin = L.j == 0 || L.u == L.us;
+      const bool end = L.j + 1 == L.nt || L.u + 1 == L.ue;
+      const int seg0 = L.base + L.h * L.nt;  // unit of the segment's tile 0
+      mt.b = L.b;
+      mt.h = L.h;
+      mt.k = L.k;
+      mt.flags = uniform(kValid | (begin ? kBegin : 0) | (end ? kEnd : 0) |
+                         (seg0 < L.us ? kBeganBefore : 0) | (L.j + 1 == L.nt ? kSegEnd : 0));
+      if (begin) {
+        if (qn_seg0 < 0) {
+          load_q(L.b, L.h, qn0);
+          qn_seg0 = uniform(L.b * H_kv + L.h);
+        } else if (kQBufs > 1 && qn_seg1 < 0) {
+          load_q(L.b, L.h, qn1);
+          qn_seg1 = uniform(L.b * H_kv + L.h);
+        }
+      }
     }
     const int t = L.j * kDecodeTile;
     int blk = block_tables[(int64_t)L.b * maxb + (t >> bs_log2)];
@@ -230,10 +330,10 @@ __global__ __launch_bounds__(64) void decode_kernel(
     const uint16_t* kt = k_cache + row0 * rs + (int64_t)L.h * D;
     const uint16_t* vt = v_cache + row0 * rs + (int64_t)L.h * D;
     const int last = L.len - 1 - t;
+    mt.rows = uniform(blk_ok ? last + 1 : 0);
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const int r = grp + i * TPI;
-      ok[i] = blk_ok && r <= last;
       const int off = (r <= last ? r : last) * rs;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -241,23 +341,71 @@ __global__ __launch_bounds__(64) void decode_kernel(
         vx[i][w] = ld16(vt + off + dofs(w));
       }
     }
-    if (lstep + 1 < R) advance(L);
-    ++lstep;
+    if (real && !switch_pending) step_unit(L);
+    pin(L);
+  };
+
+  // After the step that loaded a share's last tile: move the load cursor to
+  // the share the counter handed out, or end the wavefront's work (a counter
+  // value outside [0, dynamic shares) also ends it).
+  auto finish_share = [&](Meta& mt, const int& grab_prev) {
+    if (!switch_pending) return;
+    switch_pending = false;
+    int gv = -1;
+    if (dynamic) {
+      if (L.ue - L.us == 1) {
+        // one-tile share: ask now and wait (rare: only at the end of a level)
+        int g1 = 0;
+        if (lane == 0) g1 = atomicAdd(queue, 1);
+        gv = uniform(g1);
+      } else {
+        gv = uniform(grab_prev);
+      }
+    }
+    const int kn = gv >= 0 && gv < num_shares - W ? W + gv : num_shares;
+    int ns = T, ne = T;
+    if (kn < num_shares) sch.range(kn, ns, ne);
+    ns = uniform(ns);
+    ne = uniform(ne);
+    if (ns < T) {
+      L.k = kn;
+      L.us = ns;
+      L.ue = ne;
+      locate(L, ns);
+    } else {
+      l_active = false;
+      mt.flags |= kLast;
+    }
+    pin(L);
   };
 
   uint32_t qw[G][EPL / 2];
   float acc[G][EPL];
   float m[G], l[G];
 
-  auto begin_segment = [&]() {
-    if (qn_seg == (int64_t)C.b * H_kv + C.h) {
+  auto begin_segment = [&](const Meta& mt) {
+    const int id = mt.b * H_kv + mt.h;
+    if (qn_seg0 == id) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) qw[g][k] = qn[g][k];
-      qn_seg = -1;
+        for (int k = 0; k < EPL / 2; ++k) qw[g][k] = qn0[g][k];
+      qn_seg0 = -1;
+    } else if (kQBufs > 1 && qn_seg1 == id) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < EPL / 2; ++k) qw[g][k] = qn1[g][k];
+      qn_seg1 = -1;
     } else {
-      load_q(C.b, C.h, qw);
+      // Rare (both prefetch buffers taken): load q now and wait for it here,
+      // so that qw carries no pending load out of this branch (otherwise the
+      // first use of qw on every path would wait for this step's tile loads).
+      load_q(mt.b, mt.h, qw);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < EPL / 2; ++k) asm volatile("" : "+v"(qw[g][k]));
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -268,8 +416,7 @@ __global__ __launch_bounds__(64) void decode_kernel(
     }
   };
 
-  auto compute_tile = [&](const u32x4 (&kx)[TPL][NW], const u32x4 (&vx)[TPL][NW],
-                          const bool (&ok)[TPL]) {
+  auto compute_tile = [&](const u32x4 (&kx)[TPL][NW], const u32x4 (&vx)[TPL][NW], int rows) {
     // scores in the log2 domain
     float sc[TPL][G];
 #pragma unroll
@@ -285,7 +432,7 @@ __global__ __launch_bounds__(64) void decode_kernel(
           dsum = dot2_bf16(qw[g][4 * w + 3], kx[i][w][3], dsum);
         }
         dsum = group_sum<LPT>(dsum);
-        sc[i][g] = ok[i] ? dsum * scale_log2e : -INFINITY;
+        sc[i][g] = grp + i * TPI < rows ? dsum * scale_log2e : -INFINITY;
       }
     }
     // lazy running-max update
@@ -334,38 +481,29 @@ __global__ __launch_bounds__(64) void decode_kernel(
     }
   };
 
-  bool first_segment = true;
-  auto end_segment = [&]() {
+  auto end_segment = [&](const Meta& mt) {
     // merge the TPI lane groups (log-sum-exp); group 0 holds the result
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float M = m[g];
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) M = fmaxf(M, shfl_xor_f32(M, off));
+      const float M = cross_reduce<LPT, true>(m[g]);
       const float alpha = fast_exp2(m[g] - M);
-      float lg = l[g] * alpha;
+      l[g] = cross_reduce<LPT, false>(l[g] * alpha);
 #pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) lg += shfl_xor_f32(lg, off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float a = acc[g][e] * alpha;
-#pragma unroll
-        for (int off = LPT; off < 64; off <<= 1) a += shfl_xor_f32(a, off);
-        acc[g][e] = a;
-      }
+      for (int e = 0; e < EPL; ++e) acc[g][e] = cross_reduce<LPT, false>(acc[g][e] * alpha);
       m[g] = M;
-      l[g] = lg;
     }
-    const int64_t seg_start = C.base + (int64_t)C.h * C.nt;
-    const int64_t w_first = seg_start / U;
-    const int nparts = (int)((seg_start + C.nt - 1) / U - w_first + 1);
-    const int slot = first_segment ? 0 : 1;
-    if (wv == w_first && lane == 0)
-      ws_seg[(int64_t)C.b * H_kv + C.h] = SegInfo{nparts, (int32_t)w_first, slot, 0};
-    first_segment = false;
-    if (grp != 0) return;
-    const int64_t head0 = (int64_t)C.b * H_q + (int64_t)C.h * G;
-    if (nparts == 1) {
+    // A segment in one piece is written directly.  Otherwise its first
+    // piece records its share in k_first and its last piece in k_last; the
+    // merge combines shares k_first .. k_last.
+    const bool first_piece = !(mt.flags & kBeganBefore);
+    const bool last_piece = (mt.flags & kSegEnd) != 0;
+    if (lane == 0) {
+      int32_t* rec = reinterpret_cast<int32_t*>(ws_seg + ((int64_t)mt.b * H_kv + mt.h));
+      if (first_piece) rec[0] = mt.k;
+      if (last_piece) rec[1] = mt.k;
+    }
+    const int64_t head0 = (int64_t)mt.b * H_q + (int64_t)mt.h * G;
+    if (first_piece && last_piece) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float inv = 1.0f / l[g];
@@ -379,9 +517,12 @@ __global__ __launch_bounds__(64) void decode_kernel(
         }
       }
     } else {
+      // partial slot 0: the share's piece that began in an earlier share;
+      // slot 1: a piece that begins in this share and goes on past it
+      const int slot = first_piece ? 1 : 0;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int64_t row = (wv * 2 + slot) * G + g;
+        const int64_t row = ((int64_t)mt.k * 2 + slot) * G + g;
         float* ap = ws_acc + row * D;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -398,93 +539,111 @@ __global__ __launch_bounds__(64) void decode_kernel(
   // Ring of NBUF register buffers; the loop is unrolled NBUF times so every
   // buffer index is a compile-time constant (no register copies).
   u32x4 kbuf[NBUF][TPL][NW], vbuf[NBUF][TPL][NW];
-  bool okbuf[NBUF][TPL];
+  Meta meta[NBUF];
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) load_tile(kbuf[i], vbuf[i], okbuf[i]);
-  int64_t cstep = 0;
-  const int64_t niter = (R + NBUF - 1) / NBUF;
-  for (int64_t it = 0; it < niter; ++it) {
+  for (int i = 0; i < NBUF - 1; ++i) {
+    load_tile(kbuf[i], vbuf[i], meta[i], grab[i]);
+    finish_share(meta[i], grab[(i + NBUF - 1) % NBUF]);
+  }
+  bool done = false;
+  while (!done) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int nxt = (u + NBUF - 1) % NBUF;
-      load_tile(kbuf[nxt], vbuf[nxt], okbuf[nxt]);
-      if (cstep < R) {
-        if (cstep == 0 || C.j == 0) begin_segment();
-        compute_tile(kbuf[u], vbuf[u], okbuf[u]);
-        if (cstep + 1 == R || C.j + 1 == C.nt) end_segment();
-        if (cstep + 1 < R) advance(C);
+      const Meta mt = meta[u];
+      // take the piece's q before this step's loads may refill a q buffer
+      if ((mt.flags & (kValid | kBegin)) == (kValid | kBegin)) begin_segment(mt);
+      load_tile(kbuf[nxt], vbuf[nxt], meta[nxt], grab[nxt]);
+      if (mt.flags & kValid) {
+        compute_tile(kbuf[u], vbuf[u], mt.rows);
+        if (mt.flags & kEnd) end_segment(mt);
+        if (mt.flags & kLast) done = true;
       }
-      ++cstep;
+      finish_share(meta[nxt], grab[(nxt + NBUF - 1) % NBUF]);
     }
   }
 }
 
-// Combine the pieces of one (sequence, query head) whose segment straddled
-// wavefronts: M = max_p m_p, L = sum_p l_p 2^(m_p - M),
-// out = sum_p acc_p 2^(m_p - M) / L, pieces in wavefront order (deterministic).
-// Rows of empty sequences are written as zeros here.
+// Combine the pieces of one (sequence, query head) whose segment was cut
+// into several shares: M = max_p m_p, L = sum_p l_p 2^(m_p - M),
+// out = sum_p acc_p 2^(m_p - M) / L.  The first piece sits in partial slot 1
+// of its share, the others in slot 0.  One wavefront per output row; its 64
+// lanes take 8 pieces at a time (8 lanes of D / 8 elements per piece), and
+// the 8 piece groups are summed at the end in a fixed order, so the result is
+// deterministic.  Rows of empty sequences are written as zeros here, and the
+// share counter is reset for the next call (this kernel runs after the
+// decode kernel).
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
-    const SegInfo* __restrict__ ws_seg, const int32_t* __restrict__ context_lens,
-    uint16_t* __restrict__ out, int32_t B, int32_t H_q, int32_t G) {
-  constexpr int EPT = D / 64;
+    const SegInfo* __restrict__ ws_seg, int32_t* __restrict__ queue,
+    const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out, int32_t B,
+    int32_t H_q, int32_t G, int32_t max_shares) {
+  constexpr int EPL = D / 8;  // elements per lane of a piece group
+  if (blockIdx.x == 0 && threadIdx.x == 0) *queue = 0;
   const int lane = threadIdx.x % 64;
+  const int pg = lane / 8;   // piece group
+  const int sub = lane % 8;  // d chunk
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // b * H_q + h
   if (row >= (int64_t)B * H_q) return;
   const int b = (int)(row / H_q);
   const int hq = (int)(row - (int64_t)b * H_q);
-  uint16_t* op = out + row * D + lane * EPT;
+  uint16_t* op = out + row * D + sub * EPL;
   if (context_lens[b] <= 0) {
-    if constexpr (EPT == 2) *reinterpret_cast<uint32_t*>(op) = 0u;
-    else *op = 0;
+    if (pg == 0) {
+#pragma unroll
+      for (int w = 0; w < EPL / 8; ++w) st16(op + 8 * w, u32x4{0u, 0u, 0u, 0u});
+    }
     return;
   }
   const int H_kv = H_q / G;
   const SegInfo info = ws_seg[(int64_t)b * H_kv + hq / G];
-  if (info.nparts <= 1) return;  // written directly by the decode kernel
+  if (info.k_last <= info.k_first) return;  // one piece: written by the decode kernel
+  if (info.k_first < 0 || info.k_last >= max_shares) return;  // not from this call's layout
+  const int nparts = info.k_last - info.k_first + 1;
   const int g = hq % G;
-  auto piece = [&](int p) -> int64_t {
-    const int64_t wave = (int64_t)info.w_first + p;
-    const int slot = p == 0 ? info.slot_first : 0;
-    return (wave * 2 + slot) * G + g;
+  auto prow = [&](int p) -> int64_t {
+    const int64_t k = (int64_t)info.k_first + p;
+    return (k * 2 + (p == 0 ? 1 : 0)) * G + g;
   };
 
   float M = -INFINITY;
-  for (int p0 = 0; p0 < info.nparts; p0 += 64)
-    if (p0 + lane < info.nparts) M = fmaxf(M, ws_ml[2 * piece(p0 + lane)]);
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ws_ml[2 * prow(p)]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor_f32(M, off));
 
   float L = 0.f;
-  float o[EPT];
+  float o[EPL];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) o[e] = 0.f;
-  for (int p0 = 0; p0 < info.nparts; p0 += 64) {
-    float w = 0.f;
-    if (p0 + lane < info.nparts) {
-      const float2 st = *reinterpret_cast<const float2*>(ws_ml + 2 * piece(p0 + lane));
-      w = fast_exp2(st.x - M);
-      L += st.y * w;
-    }
-    const int cnt = min(64, info.nparts - p0);
-#pragma unroll 8
-    for (int j = 0; j < cnt; ++j) {
-      const float wj =
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-      const float* src = ws_acc + piece(p0 + j) * D + lane * EPT;
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+#pragma unroll 2
+  for (int p = pg; p < nparts; p += 8) {
+    const int64_t r = prow(p);
+    const float2 st = *reinterpret_cast<const float2*>(ws_ml + 2 * r);
+    const float w = fast_exp2(st.x - M);
+    L += st.y * w;
+    const float* src = ws_acc + r * D + sub * EPL;
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) o[e] += src[e] * wj;
+    for (int e = 0; e < EPL; e += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+      o[e + 0] += v[0] * w;
+      o[e + 1] += v[1] * w;
+      o[e + 2] += v[2] * w;
+      o[e + 3] += v[3] * w;
     }
   }
+  L = cross_reduce<8, false>(L);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L += shfl_xor_f32(L, off);
+  for (int e = 0; e < EPL; ++e) o[e] = cross_reduce<8, false>(o[e]);
+  if (pg != 0) return;
   const float inv = 1.0f / L;
-  if constexpr (EPT == 2) {
-    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(o[0] * inv, o[1] * inv);
-  } else {
-    const uint32_t pk = pack_bf16x2(o[0] * inv, 0.f);
-    *op = (uint16_t)(pk & 0xffffu);
+#pragma unroll
+  for (int w = 0; w < EPL / 8; ++w) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[k] = pack_bf16x2(o[8 * w + 2 * k] * inv, o[8 * w + 2 * k + 1] * inv);
+    st16(op + 8 * w, v);
   }
 }
 
@@ -498,7 +657,7 @@ static int ilog2(int x) {
 
 // One wavefront per resident slot of the current device (cached per device
 // and kernel variant).
-template <int D, int G, int EPL, int NBUF>
+template <int D, int G, int EPL, int NBUF, int WPE>
 static int resident_waves() {
   static int cached[64] = {0};
   int dev = 0;
@@ -508,7 +667,7 @@ static int resident_waves() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, EPL, NBUF>, 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, EPL, NBUF, WPE>, 64,
                                                      0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 8;
@@ -522,17 +681,17 @@ template <typename F>
 static bool dispatch(int d, int G, F& f) {
   if (d == 128) {
     switch (G) {
-      case 1: f.template run<128, 1, 16, 3>(); return true;
-      case 2: f.template run<128, 2, 16, 3>(); return true;
-      case 4: f.template run<128, 4, 8, 3>(); return true;
-      case 8: f.template run<128, 8, 8, 2>(); return true;
+      case 1: f.template run<128, 1, 16, 3, 2>(); return true;
+      case 2: f.template run<128, 2, 16, 3, 2>(); return true;
+      case 4: f.template run<128, 4, 8, 3, 2>(); return true;
+      case 8: f.template run<128, 8, 8, 2, 1>(); return true;
     }
   } else if (d == 64) {
     switch (G) {
-      case 1: f.template run<64, 1, 8, 3>(); return true;
-      case 2: f.template run<64, 2, 8, 3>(); return true;
-      case 4: f.template run<64, 4, 8, 3>(); return true;
-      case 8: f.template run<64, 8, 8, 2>(); return true;
+      case 1: f.template run<64, 1, 8, 3, 2>(); return true;
+      case 2: f.template run<64, 2, 8, 3, 2>(); return true;
+      case 4: f.template run<64, 4, 8, 3, 2>(); return true;
+      case 8: f.template run<64, 8, 8, 2, 1>(); return true;
     }
   }
   return false;
@@ -540,11 +699,29 @@ static bool dispatch(int d, int G, F& f) {
 
 struct WaveQuery {
   int waves = 0;
-  template <int D, int G, int EPL, int NBUF>
-  void run() { waves = resident_waves<D, G, EPL, NBUF>(); }
+  template <int D, int G, int EPL, int NBUF, int WPE>
+  void run() { waves = resident_waves<D, G, EPL, NBUF, WPE>(); }
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace: two fp32 partial slots (acc[d], then (m, l)) per query head of
+// a group for every share of the schedule (kLevels * W shares), one SegInfo
+// per (sequence, KV head), and the share counter in its own 256-byte line.
+struct WorkspaceLayout {
+  size_t acc, ml, seg, queue, total;
+};
+static WorkspaceLayout workspace_layout(int32_t B, int32_t H_kv, int32_t G, int32_t d,
+                                        int32_t waves) {
+  WorkspaceLayout w;
+  const size_t rows = (size_t)ShareSchedule::max_shares(waves) * 2 * G;
+  w.acc = 0;
+  w.ml = align256(rows * d * sizeof(float));
+  w.seg = w.ml + align256(rows * 2 * sizeof(float));
+  w.queue = w.seg + align256((size_t)B * H_kv * sizeof(SegInfo));
+  w.total = w.queue + 256;
+  return w;
+}
 
 DecodePlan decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t block_size,
                        int32_t max_blocks_per_seq) {
@@ -555,9 +732,7 @@ DecodePlan decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t 
   WaveQuery wq;
   if (!dispatch(d, G, wq)) return p;
   p.num_waves = wq.waves;
-  const size_t rows = (size_t)wq.waves * 2 * G;  // two partial slots per wavefront
-  p.workspace_bytes = align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) +
-                      (size_t)B * H_kv * sizeof(SegInfo);
+  p.workspace_bytes = workspace_layout(B, H_kv, G, d, wq.waves).total;
   return p;
 }
 
@@ -569,12 +744,13 @@ struct DecodeLaunch {
   uint16_t* out;
   float *wa, *wm;
   SegInfo* wseg;
+  int32_t* queue;
   int32_t B, H_kv, nb, bsl, maxb;
   float sl2e;
-  template <int D, int G, int EPL, int NBUF>
+  template <int D, int G, int EPL, int NBUF, int WPE>
   void run() {
-    hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF>), grid, dim3(64), 0, st, q, kc, vc, bt, cl,
-                       out, wa, wm, wseg, B, H_kv, nb, bsl, maxb, sl2e);
+    hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF, WPE>), grid, dim3(64), 0, st, q, kc, vc, bt, cl,
+                       out, wa, wm, wseg, queue, B, H_kv, nb, bsl, maxb, sl2e);
   }
 };
 
@@ -585,26 +761,27 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
                          const DecodePlan& plan, hipStream_t stream) {
   const int G = H_q / H_kv;
-  const size_t rows = (size_t)plan.num_waves * 2 * G;
+  const WorkspaceLayout wl = workspace_layout(B, H_kv, G, d, plan.num_waves);
   char* ws = static_cast<char*>(workspace);
-  float* wa = reinterpret_cast<float*>(ws);
-  float* wm = reinterpret_cast<float*>(ws + align256(rows * d * sizeof(float)));
-  SegInfo* wseg = reinterpret_cast<SegInfo*>(ws + align256(rows * d * sizeof(float)) +
-                                             align256(rows * 2 * sizeof(float)));
+  float* wa = reinterpret_cast<float*>(ws + wl.acc);
+  float* wm = reinterpret_cast<float*>(ws + wl.ml);
+  SegInfo* wseg = reinterpret_cast<SegInfo*>(ws + wl.seg);
+  int32_t* queue = reinterpret_cast<int32_t*>(ws + wl.queue);
   DecodeLaunch lf{dim3((unsigned)plan.num_waves), stream, q, k_cache, v_cache, block_tables,
-                  context_lens, out, wa, wm, wseg, B, H_kv, num_blocks, ilog2(block_size),
+                  context_lens, out, wa, wm, wseg, queue, B, H_kv, num_blocks, ilog2(block_size),
                   max_blocks_per_seq, softmax_scale * 1.4426950408889634f};
   if (!dispatch(d, G, lf)) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nrows = (int64_t)B * H_q;
+  const int32_t max_shares = (int32_t)ShareSchedule::max_shares(plan.num_waves);
   dim3 mgrid((unsigned)((nrows + 3) / 4));
   if (d == 128)
     hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(256), 0, stream, wa, wm, wseg,
-                       context_lens, out, B, H_q, G);
+                       queue, context_lens, out, B, H_q, G, max_shares);
   else
     hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(256), 0, stream, wa, wm, wseg,
-                       context_lens, out, B, H_q, G);
+                       queue, context_lens, out, B, H_q, G, max_shares);
   return hipGetLastError();
 }
 

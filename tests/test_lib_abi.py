@@ -96,12 +96,15 @@ def test_attention_argument_checks_before_launch():
 
 def test_workspace_size_formula():
     lib = _lib.load()
-    # two partial slots per resident wavefront, plus 16 bytes per (sequence, KV head)
-    a = lib.pkv_decode_workspace_size(4, 4, 2, 64, 16, 3)
-    b = lib.pkv_decode_workspace_size(5, 4, 2, 64, 16, 3)
-    assert a > 0 and b - a == 2 * 16
-    c = lib.pkv_decode_workspace_size(4, 8, 2, 64, 16, 3)  # G = 4: twice the partial rows
+    # partial slots per share of the schedule, plus 16 bytes per (sequence, KV head)
+    # (256-byte aligned) and the share counter's line
+    a = lib.pkv_decode_workspace_size(16, 4, 2, 64, 16, 3)
+    b = lib.pkv_decode_workspace_size(32, 4, 2, 64, 16, 3)
+    assert a > 0 and b - a == 16 * 2 * 16
+    c = lib.pkv_decode_workspace_size(16, 8, 2, 64, 16, 3)  # G = 4: twice the partial rows
     assert c > a
+    # the schedule counts units in int32: tables too wide for that are refused
+    assert lib.pkv_decode_workspace_size(4096, 16, 8, 128, 256, 1 << 16) == 0
     assert lib.pkv_decode_workspace_size(4, 4, 2, 96, 16, 3) == 0  # unsupported d
     assert lib.pkv_decode_workspace_size(4, 6, 4, 64, 16, 3) == 0  # H_q % H_kv
 
