@@ -68,7 +68,7 @@ def measured_traffic(workload: str):
     if not rec:
         return None
     h = hashlib.sha256()
-    for f in ("pkv_decode.hip", "device_common.h"):
+    for f in ("pkv_decode.hip", "device_common.h", "decode_schedule.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_110_amd", "csrc", f), "rb").read())
     if h.hexdigest() != rec["decode_source_sha256"]:
         return None

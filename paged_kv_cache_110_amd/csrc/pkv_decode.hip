@@ -11,11 +11,11 @@
 // kernel is organised around streaming K/V at full bandwidth until the very
 // end of the call, not around MFMA:
 //  - work is the flattened list of 16-token tiles of every (sequence, KV head)
-//    segment.  Exactly one wavefront is launched per resident slot of the GPU,
-//    and each takes an equal contiguous share of that list, so every slot
-//    streams for the same time and the call ends sharply (with one wavefront
-//    per fixed-size split instead, the last round of wavefronts runs on a
-//    partly empty GPU);
+//    segment.  Exactly one wavefront is launched per resident slot of the GPU.
+//    Each first streams a static share of the list, then takes shrinking
+//    shares from an atomic counter (decode_schedule.h): the two wavefronts of
+//    a SIMD progress at very different rates, so equal static shares would
+//    leave the call waiting for the slowest;
 //  - 16 divides every supported block size and tiles start at multiples of 16,
 //    so a tile never crosses a page (the devpress page's point about read
 //    lengths dividing the block size): its physical block id is one scalar load
@@ -34,10 +34,10 @@
 //    sum, rescaled output) per lane group, in the log2 domain with
 //    scale*log2(e) folded in; the rescale is lazy (only when some lane's tile
 //    maximum exceeds its running maximum by more than 2^8), exact math;
-//  - a segment that lies inside one wavefront's share is finished in place and
-//    written as bf16.  Only a wavefront's first and last segment can straddle
-//    wavefronts: those write an fp32 partial (m, l, acc[d]) to one of the
-//    wavefront's two partial slots, and decode_merge_kernel combines them.
+//  - a segment that lies inside one share is finished in place and written as
+//    bf16.  A segment cut by share boundaries writes an fp32 partial
+//    (m, l, acc[d]) per piece into its share's partial slots, and
+//    decode_merge_kernel combines the pieces in share order.
 #include <stdlib.h>
 
 #include "decode_schedule.h"
