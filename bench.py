@@ -203,6 +203,32 @@ def cpu_baseline(name, budget_s, log):
                 ms_per_step=round(step_s * 1e3, 2))
 
 
+def run_packed(steps, warmup, torch, pkv, log):
+    """Varlen causal prefill over packed K/V (no block table, no prefix): q/k/v
+    are row views of one fused projection buffer."""
+    from workloads.packed import PACKED_PREFILL as cfg, make_packed, split_fused
+
+    lens, cu, fused = make_packed("cuda")
+    q, k, v = split_fused(fused)
+    out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    scale = 1.0 / math.sqrt(cfg["d"])
+    mx = max(lens)
+    for _ in range(warmup):
+        pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    for _ in range(steps):
+        with timer.span("attn"):
+            pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("attn")
+    fl = 4 * cfg["d"] * cfg["H_q"] * sum(n * (n + 1) // 2 for n in lens)
+    tf = fl / (ms * 1e-3) / 1e12
+    return dict(workload="packed_prefill", B=cfg["B"], tokens=sum(lens), attn_ms=round(ms, 4),
+                prefill_tflops=round(tf, 2), prefill_pct_mfma_peak=round(100 * tf / BF16_PEAK_TFLOPS, 2),
+                tokens_per_s=round(sum(lens) / (ms * 1e-3), 1), flops=fl)
+
+
 def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
     """Plain device copy (torch copy_) and plain read (torch sum) of a buffer of known
     size: the achievable-bandwidth reference for the roofline, and the known-size
@@ -293,6 +319,8 @@ def main() -> int:
 
     secondary = {}
     if not args.no_secondary:
+        secondary["packed_prefill"] = run_packed(max(5, args.steps // 2), 2, torch, pkv, log)
+        log(json.dumps(secondary["packed_prefill"]))
         for name in ["long_decode", "prefix_prefill", "full_step"]:
             if name == args.workload:
                 continue

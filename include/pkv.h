@@ -181,8 +181,13 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
  *   max_seqlen_k  host bound on nk (informational; keys are clamped to the table)
  *   other arguments as for pkv_decode.
  * Query rows at or beyond total_q are never written.
- * PKV_EINVAL / PKV_EUNSUPPORTED as for pkv_decode, plus total_q < 0 or
- * max_seqlen_q < 0.  B == 0 or max_seqlen_q == 0 enqueues nothing.
+ * Precision: q.k products and all sums in fp32; the probabilities and V enter
+ * the PV product as fp16, so every V value must lie within fp16's range
+ * (|v| <= 65504; larger values give non-finite rows); V values under 2^-14 in
+ * magnitude are rounded to fp16 subnormals (absolute error below 2^-25).
+ * PKV_EINVAL / PKV_EUNSUPPORTED as for pkv_decode, plus total_q < 0,
+ * max_seqlen_q < 0 or B > 65535.  B == 0, total_q == 0 or max_seqlen_q == 0
+ * enqueues nothing.
  */
 pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_tables,
@@ -192,6 +197,40 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
                               int32_t num_blocks, int32_t block_size,
                               int32_t max_blocks_per_seq, float softmax_scale,
                               hipStream_t stream);
+
+/*
+ * Varlen causal prefill over packed, non-paged K/V (devpress page, "如何适配
+ * 不同请求不同序列长度": the varlen call without a block table, keys of all
+ * sequences stacked on the token axis and addressed by cu_seqlens_k).
+ * Sequence b has nq = cu_seqlens_q[b+1]-cu_seqlens_q[b] queries and
+ * nk = cu_seqlens_k[b+1]-cu_seqlens_k[b] keys (nq <= nk; nq == nk is the
+ * no-prefix case); query i sits at position nk - nq + i and attends keys
+ * 0 .. nk - nq + i (causal, bottom-right aligned):
+ *   out[cu_q[b]+i, h, :] = softmax_j( q . k[cu_k[b]+j, h/G] * scale ) v[cu_k[b]+j, h/G]
+ *   q      device, [total_q, H_q, d] bf16 rows q_stride elements apart
+ *   k, v   device, [total_k, H_kv, d] bf16 rows k_stride / v_stride elements apart
+ *          (heads and d contiguous; e.g. views of a fused QKV projection)
+ *   out    device, [total_q, H_q, d] bf16, contiguous
+ *   cu_seqlens_q, cu_seqlens_k   device, [B+1] int32, cu_seqlens_q[0] == 0,
+ *          cu_seqlens_q[B] == total_q, cu_seqlens_k[B] <= total_k
+ *   max_seqlen_q  host bound on nq (sizes the grid; sequences beyond it are cut)
+ *   max_seqlen_k  host bound on nk (informational)
+ * Key rows outside [0, total_k) are never read (rows are clamped; the results
+ * of calls that violate the cu_seqlens preconditions are unspecified).
+ * Precision as for pkv_prefill_varlen (V within fp16's range).
+ * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, a stride
+ * below the row size or not a multiple of 8, misaligned pointers, B < 0,
+ * B > 65535, total_q < 0, total_k < 0, or total_k == 0 with work to do.
+ * PKV_EUNSUPPORTED: d not in {64, 128} or H_q/H_kv not in {1, 2, 4, 8}.
+ * B == 0, total_q == 0 or max_seqlen_q == 0 enqueues nothing.
+ */
+pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride, const void* k,
+                                     int64_t k_stride, const void* v, int64_t v_stride,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t B, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H_q,
+                                     int32_t H_kv, int32_t d, float softmax_scale,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

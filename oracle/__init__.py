@@ -165,6 +165,27 @@ class Oracle:
         return torch.from_numpy(out)
 
 
+    def prefill_packed(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q,
+                       cu_seqlens_k, softmax_scale: float) -> torch.Tensor:
+        """Varlen causal prefill over packed K/V [total_k, H_kv, d]: key j of
+        sequence b is token row cu_seqlens_k[b] + j (devpress page, the varlen
+        call without a block table).  The same attention as prefill(), read
+        through a one-token-per-block table that maps key j of sequence b to
+        row cu_seqlens_k[b] + j."""
+        total_k, H_kv, d = k.shape
+        ck = _i32(cu_seqlens_k)
+        B = ck.shape[0] - 1
+        nk = ck[1:] - ck[:-1]
+        width = max(1, int(nk.max()) if B > 0 else 1)
+        table = np.full((max(B, 0), width), -1, dtype=np.int32)
+        for b in range(B):
+            table[b, : nk[b]] = np.arange(ck[b], ck[b + 1], dtype=np.int32)
+        kc = k.contiguous().reshape(total_k, 1, H_kv, d)
+        vc = v.contiguous().reshape(total_k, 1, H_kv, d)
+        return self.prefill(q.contiguous(), kc, vc, table, cu_seqlens_q, cu_seqlens_k,
+                            softmax_scale)
+
+
 _DEFAULT: Optional[Oracle] = None
 
 

@@ -26,7 +26,7 @@ from ._lib import EXPORTS, LIB_PATH, PkvError, check, load
 
 __all__ = [
     "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
-    "PkvError", "LIB_PATH", "EXPORTS", "version",
+    "prefill_varlen_packed", "PkvError", "LIB_PATH", "EXPORTS", "version",
 ]
 
 
@@ -176,4 +176,42 @@ def prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(cu_seqlens_q),
         _ptr(cu_seqlens_k), B, total_q, int(max_seqlen_q), int(max_seqlen_k), H_q, H_kv, d, nb, bs,
         int(block_tables.shape[1]), scale, _stream(stream)))
+    return out
+
+
+def _rows(t: torch.Tensor, name: str, H: int, d: int) -> None:
+    _need(t.dim() == 3 and tuple(t.shape[1:]) == (H, d) and t.dtype == torch.bfloat16
+          and t.is_cuda, f"{name} must be a bf16 GPU tensor [tokens, {H}, {d}]")
+    _need(t.stride(2) == 1 and t.stride(1) == d, f"{name}: head and d dims must be contiguous")
+
+
+def prefill_varlen_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                          max_seqlen_q: int, max_seqlen_k: int,
+                          softmax_scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Varlen causal prefill over packed K/V [total_k, H_kv, d] (token rows of all
+    sequences stacked, addressed by cu_seqlens_k); q [total_q, H_q, d] -> out (bf16).
+    q, k and v may be row-strided views (e.g. of a fused QKV projection)."""
+    _need(q.dim() == 3 and k.dim() == 3, "q/k/v must be [tokens, heads, d]")
+    H_q, d = int(q.shape[1]), int(q.shape[2])
+    H_kv = int(k.shape[1])
+    _rows(q, "q", H_q, d)
+    _rows(k, "k", H_kv, d)
+    _rows(v, "v", H_kv, d)
+    _need(v.shape[0] == k.shape[0], "k and v must have the same number of rows")
+    _dev_i32(cu_seqlens_q, "cu_seqlens_q")
+    _dev_i32(cu_seqlens_k, "cu_seqlens_k")
+    B = int(cu_seqlens_q.shape[0]) - 1
+    _need(cu_seqlens_k.shape == cu_seqlens_q.shape and B >= 0, "cu_seqlens must be [B+1]")
+    total_q, total_k = int(q.shape[0]), int(k.shape[0])
+    if out is None:
+        out = torch.empty((total_q, H_q, d), dtype=q.dtype, device=q.device)
+    _need(out.shape == (total_q, H_q, d) and out.dtype == q.dtype and out.is_contiguous(),
+          "bad out")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    check("pkv_prefill_varlen_packed", load().pkv_prefill_varlen_packed(
+        _ptr(out), _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, total_q, total_k, int(max_seqlen_q),
+        int(max_seqlen_k), H_q, H_kv, d, scale, _stream(stream)))
     return out

@@ -22,6 +22,7 @@ EXPORTS = (
     "pkv_decode_workspace_size",
     "pkv_decode",
     "pkv_prefill_varlen",
+    "pkv_prefill_varlen_packed",
 )
 
 
@@ -61,6 +62,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_prefill_varlen.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                        I32, I32, I32, F, P]
     lib.pkv_prefill_varlen.restype = ctypes.c_int
+    lib.pkv_prefill_varlen_packed.argtypes = [P, P, I64, P, I64, P, I64, P, P, I32, I32, I32, I32,
+                                              I32, I32, I32, I32, F, P]
+    lib.pkv_prefill_varlen_packed.restype = ctypes.c_int
     _lib = lib
     return lib
 

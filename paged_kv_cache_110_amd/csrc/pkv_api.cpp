@@ -191,4 +191,29 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
       max_blocks_per_seq, softmax_scale, stream));
 }
 
+pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride, const void* k,
+                                     int64_t k_stride, const void* v, int64_t v_stride,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t B, int32_t total_q, int32_t total_k,
+                                     int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H_q,
+                                     int32_t H_kv, int32_t d, float softmax_scale,
+                                     hipStream_t stream) {
+  (void)max_seqlen_k;
+  if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0) return PKV_EINVAL;
+  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return PKV_OK;
+  if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k) return PKV_EINVAL;
+  if (H_q <= 0 || H_kv <= 0 || d <= 0 || H_q % H_kv != 0 || total_k <= 0) return PKV_EINVAL;
+  if (B > 65535) return PKV_EINVAL;
+  const int64_t qrow = (int64_t)H_q * d, kvrow = (int64_t)H_kv * d;
+  if (q_stride < qrow || k_stride < kvrow || v_stride < kvrow) return PKV_EINVAL;
+  if (q_stride % 8 || k_stride % 8 || v_stride % 8) return PKV_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return PKV_EINVAL;
+  if (!supported_d(d) || !supported_group(H_q, H_kv)) return PKV_EUNSUPPORTED;
+  return launch_status(pkv::launch_prefill_packed(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q), q_stride,
+      static_cast<const uint16_t*>(k), k_stride, static_cast<const uint16_t*>(v), v_stride,
+      cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, max_seqlen_q, H_q, H_kv, d, softmax_scale,
+      stream));
+}
+
 }  // extern "C"

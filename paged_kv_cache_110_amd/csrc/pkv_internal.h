@@ -35,4 +35,12 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_ca
                           int32_t d, int32_t num_blocks, int32_t block_size,
                           int32_t max_blocks_per_seq, float softmax_scale, hipStream_t stream);
 
+// Varlen causal prefill over packed (non-paged) K/V rows; strides in elements.
+hipError_t launch_prefill_packed(uint16_t* out, const uint16_t* q, int64_t q_stride,
+                                 const uint16_t* k, int64_t k_stride, const uint16_t* v,
+                                 int64_t v_stride, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t B, int32_t total_q,
+                                 int32_t total_k, int32_t max_seqlen_q, int32_t H_q, int32_t H_kv,
+                                 int32_t d, float softmax_scale, hipStream_t stream);
+
 }  // namespace pkv

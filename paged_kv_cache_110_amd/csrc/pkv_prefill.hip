@@ -21,8 +21,10 @@
 //  - S^T = K Q^T puts keys on the MFMA M side and the packed query rows on N,
 //    so every lane ends up owning scores of a single query row: the softmax
 //    statistics are per lane (plus one exchange with lane l^32);
-//  - O^T += V^T P^T: the P operand is the lane's own scores (rounded to bf16)
-//    and the V^T operand comes straight from the row-major V tile with
+//  - O^T += V^T P^T: the P operand is the lane's own scores, rounded to fp16
+//    (bf16 would leave outputs of magnitude 2..4 close to the 1e-2 error
+//    bar), and the V^T operand comes straight from the row-major V tile, kept
+//    in LDS as fp16 (exact for bf16 values of normal fp16 range), with
 //    ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit elements;
 //  - online softmax in the log2 domain with the same lazy rescale as decode;
 //    only tiles that cross the diagonal are masked;
@@ -35,6 +37,21 @@ namespace pkv {
 
 constexpr int kPrefillBN = 64;  // keys per tile
 constexpr float kPrefillLazy = 8.0f;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 8 bf16 -> 8 fp16 (round to nearest even).  V tiles are kept in LDS as fp16
+// so that P can be rounded to fp16 (8x finer than bf16) for the PV product.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f16x2 h = {(_Float16)bf16_lo(w[k]), (_Float16)bf16_hi(w[k])};
+    r[k] = __builtin_bit_cast(uint32_t, h);
+  }
+  return r;
+}
 
 __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -53,13 +70,20 @@ __device__ __forceinline__ int swz(int row) {
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-template <int D, int G>
+// PAGED: keys come from the paged cache through block_tables (k_cache/v_cache
+// [num_blocks, block_size, H_kv, d]).  Otherwise (the no-prefix form of the
+// devpress page's varlen call) keys of sequence b are the token rows
+// cu_k[b] .. cu_k[b+1]-1 of packed K/V [total_k, H_kv, d]; num_blocks then
+// carries total_k, and block_tables, bs_log2 and maxb are unused.  q, k and v
+// rows are q_stride / k_stride / v_stride elements apart (views of a fused
+// projection), heads and d contiguous.
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, uint16_t* __restrict__ out,
     int32_t total_q, int32_t H_kv, int32_t num_blocks, int32_t bs_log2, int32_t maxb,
-    float scale_log2e) {
+    int64_t q_stride, int64_t k_stride, int64_t v_stride, float scale_log2e) {
   constexpr int BN = kPrefillBN;
   constexpr int QPW = 32 / G;          // query positions per wavefront
   constexpr int QPB = 4 * QPW;         // query positions per workgroup
@@ -81,9 +105,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   const int qs = cu_q[b];
   const int nq = cu_q[b + 1] - qs;
-  const int cap = maxb << bs_log2;
+  const int cap = PAGED ? (maxb << bs_log2) : num_blocks;
   int nk = cu_k[b + 1] - cu_k[b];
   nk = nk > cap ? cap : nk;
+  const int kb0 = PAGED ? 0 : cu_k[b];  // packed: first key row of the sequence
   if (nq <= 0 || nk < nq || qs < 0) return;
   const int c = nk - nq;
   const int nqt = (nq + QPB - 1) / QPB;
@@ -104,7 +129,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   bf16x8 qf[KS];
   {
-    const uint16_t* qp = q + (((int64_t)qs + qq) * H_q + head) * D + 8 * half;
+    const uint16_t* qp = q + ((int64_t)qs + qq) * q_stride + (int64_t)head * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = row_ok ? ld16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
@@ -122,8 +147,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   // cooperative tile loader: thread -> (chunk ch, rows r0 + RPP * p)
   const int ch = tid % CPR;
   const int r0 = tid / CPR;
-  const int row_stride = H_kv * D;  // elements between token rows of the cache
-  const int goff = r0 * row_stride + ch * 8;  // element offset of this thread's first row
+  const int64_t row_stride = k_stride;  // elements between K token rows (paged: == v_stride)
+  const int64_t goff = r0 * row_stride + ch * 8;  // element offset of this thread's first row
+  const int64_t goff_v = r0 * v_stride + ch * 8;
   // the LDS slot of this thread's chunk; rows r0 + RPP * p share their low four bits
   const int soff = r0 * D + ((ch ^ swz<CPR>(r0)) << 3);
   // K operand reads: row kb * 32 + mrow, logical chunk 2 * ks + half.  The row
@@ -158,6 +184,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   // out-of-range block id, read valid memory and are zeroed when stashed.
   const bool tile_in_block = bs_log2 >= 6;
   auto load_tile = [&](int kt) {
+    if constexpr (!PAGED) {
+      // consecutive token rows; rows past kend re-read the last key (zeroed when stashed)
+      // (rows are also kept inside [0, total_k) whatever cu_k holds)
+      const int j0 = kt * BN;
+      if (j0 + BN <= kend && kb0 >= 0 && (int64_t)kb0 + j0 + BN <= num_blocks) {
+        const uint16_t* kb = khead + ((int64_t)kb0 + j0) * k_stride;
+        const uint16_t* vb = vhead + ((int64_t)kb0 + j0) * v_stride;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          kok[p] = true;
+          kr[p] = ld16(kb + (int64_t)RPP * p * k_stride + goff);
+          vr[p] = ld16(vb + (int64_t)RPP * p * v_stride + goff_v);
+        }
+        full_next = true;
+      } else {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          const int j = j0 + r0 + RPP * p;
+          kok[p] = j < kend;
+          int64_t row = (int64_t)kb0 + (j < kend ? j : kend - 1);
+          row = row < 0 ? 0 : (row >= num_blocks ? num_blocks - 1 : row);
+          kr[p] = ld16(khead + row * k_stride + ch * 8);
+          vr[p] = ld16(vhead + row * v_stride + ch * 8);
+        }
+        full_next = false;
+      }
+      return;
+    }
     if (tile_in_block) {
       int blk = table[(kt * BN) >> bs_log2];  // kt * BN < kend: a valid entry
       const bool blk_ok = (unsigned)blk < (unsigned)num_blocks;
@@ -169,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       for (int p = 0; p < PASSES; ++p) {
         kok[p] = blk_ok && kt * BN + r0 + RPP * p < kend;
         kr[p] = ld16(kb + (int64_t)RPP * p * row_stride + goff);
-        vr[p] = ld16(vb + (int64_t)RPP * p * row_stride + goff);
+        vr[p] = ld16(vb + (int64_t)RPP * p * row_stride + goff_v);
       }
       full_next = blk_ok && kt * BN + BN <= kend;
     } else {
@@ -185,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         kok[p] = j < kend && (unsigned)blk[p] < (unsigned)num_blocks;
         const int64_t row = kok[p] ? (((int64_t)blk[p] << bs_log2) + (j & bmask)) : 0;
         kr[p] = ld16(khead + row * row_stride + ch * 8);
-        vr[p] = ld16(vhead + row * row_stride + ch * 8);
+        vr[p] = ld16(vhead + row * v_stride + ch * 8);
       }
       full_next = false;
     }
@@ -196,14 +250,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         *reinterpret_cast<u32x4*>(kt_lds + soff + RPP * p * D) = kr[p];
-        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = vr[p];
+        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = bf16x8_to_f16x8(vr[p]);
       }
     } else {
       const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         *reinterpret_cast<u32x4*>(kt_lds + soff + RPP * p * D) = kok[p] ? kr[p] : zero;
-        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = kok[p] ? vr[p] : zero;
+        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) =
+            kok[p] ? bf16x8_to_f16x8(vr[p]) : zero;
       }
     }
   };
@@ -248,8 +303,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
-    // P = 2^(s * scale * log2 e - m), rounded to bf16 for the PV product
-    bf16x8 pf[2][2];
+    // P = 2^(s * scale * log2 e - m) (at most 2^8 with the lazy rescale),
+    // rounded to fp16 for the PV product
+    f16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -258,7 +314,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         for (int e = 0; e < 8; ++e) {
           const float p = fast_exp2(__builtin_fmaf(sacc[kb][8 * s2 + e], scale_log2e, -m));
           l += p;
-          pf[kb][s2][e] = (__bf16)p;
+          pf[kb][s2][e] = (_Float16)p;
         }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -271,8 +327,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           const i16x4 vb = lds_read_tr16(vt_lds + voff[db][1] + rofs);
           typedef short i16x8 __attribute__((ext_vector_type(8)));
           const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8),
-                                                          pf[kb][s2], o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, v8),
+                                                         pf[kb][s2], o[db], 0, 0, 0);
         }
   };
 
@@ -306,36 +362,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   }
 }
 
-static int ilog2p(int x) {
-  int r = 0;
-  while ((1 << r) < x) ++r;
-  return r;
-}
-
-template <int D, int G>
+template <int D, int G, bool PAGED>
 static void launch_pf(dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* kc,
                       const uint16_t* vc, const int32_t* bt, const int32_t* cq, const int32_t* ck,
                       uint16_t* out, int32_t total_q, int32_t H_kv, int32_t nb, int32_t bsl,
-                      int32_t maxb, float sl2e) {
-  hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(256), 0, st, q, kc, vc, bt, cq, ck, out,
-                     total_q, H_kv, nb, bsl, maxb, sl2e);
+                      int32_t maxb, int64_t qs, int64_t ks, int64_t vs, float sl2e) {
+  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED>), grid, dim3(256), 0, st, q, kc, vc, bt, cq, ck,
+                     out, total_q, H_kv, nb, bsl, maxb, qs, ks, vs, sl2e);
 }
 
-hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
-                          const uint16_t* v_cache, const int32_t* block_tables,
-                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t B,
-                          int32_t total_q, int32_t max_seqlen_q, int32_t H_q, int32_t H_kv,
-                          int32_t d, int32_t num_blocks, int32_t block_size,
-                          int32_t max_blocks_per_seq, float softmax_scale, hipStream_t stream) {
+template <bool PAGED>
+static hipError_t launch_prefill_any(uint16_t* out, const uint16_t* q, const uint16_t* k,
+                                     const uint16_t* v, const int32_t* block_tables,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                     int32_t B, int32_t total_q, int32_t max_seqlen_q, int32_t H_q,
+                                     int32_t H_kv, int32_t d, int32_t num_blocks, int32_t bsl,
+                                     int32_t maxb, int64_t qs, int64_t ks, int64_t vs,
+                                     float softmax_scale, hipStream_t stream) {
   const int G = H_q / H_kv;
   const int qpb = 4 * (32 / G);
   const unsigned zt = (unsigned)((max_seqlen_q + qpb - 1) / qpb);
   dim3 grid((unsigned)H_kv, (unsigned)B, zt);
-  const int bsl = ilog2p(block_size);
   const float sl2e = softmax_scale * 1.4426950408889634f;
-#define PKV_PF(DD, GG)                                                                       \
-  launch_pf<DD, GG>(grid, stream, q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k, \
-                    out, total_q, H_kv, num_blocks, bsl, max_blocks_per_seq, sl2e)
+#define PKV_PF(DD, GG)                                                                        \
+  launch_pf<DD, GG, PAGED>(grid, stream, q, k, v, block_tables, cu_seqlens_q, cu_seqlens_k, out, \
+                           total_q, H_kv, num_blocks, bsl, maxb, qs, ks, vs, sl2e)
   if (d == 128) {
     switch (G) {
       case 1: PKV_PF(128, 1); break;
@@ -353,6 +404,36 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_ca
   }
 #undef PKV_PF
   return hipGetLastError();
+}
+
+static int ilog2p(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                          const uint16_t* v_cache, const int32_t* block_tables,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t B,
+                          int32_t total_q, int32_t max_seqlen_q, int32_t H_q, int32_t H_kv,
+                          int32_t d, int32_t num_blocks, int32_t block_size,
+                          int32_t max_blocks_per_seq, float softmax_scale, hipStream_t stream) {
+  const int64_t row = (int64_t)H_kv * d;
+  return launch_prefill_any<true>(out, q, k_cache, v_cache, block_tables, cu_seqlens_q,
+                                  cu_seqlens_k, B, total_q, max_seqlen_q, H_q, H_kv, d,
+                                  num_blocks, ilog2p(block_size), max_blocks_per_seq,
+                                  (int64_t)H_q * d, row, row, softmax_scale, stream);
+}
+
+hipError_t launch_prefill_packed(uint16_t* out, const uint16_t* q, int64_t q_stride,
+                                 const uint16_t* k, int64_t k_stride, const uint16_t* v,
+                                 int64_t v_stride, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t B, int32_t total_q,
+                                 int32_t total_k, int32_t max_seqlen_q, int32_t H_q, int32_t H_kv,
+                                 int32_t d, float softmax_scale, hipStream_t stream) {
+  return launch_prefill_any<false>(out, q, k, v, nullptr, cu_seqlens_q, cu_seqlens_k, B, total_q,
+                                   max_seqlen_q, H_q, H_kv, d, total_k, 0, 0, q_stride, k_stride,
+                                   v_stride, softmax_scale, stream);
 }
 
 }  // namespace pkv

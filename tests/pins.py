@@ -255,6 +255,41 @@ def pin_shared_prefix(orc):
     assert not torch.equal(out[0:3], out[10:13])
 
 
+def pin_packed_prefill_equals_library(orc):
+    """Varlen prefill over packed K/V (token rows of all sequences stacked, the
+    varlen call without a block table), with and without a prefix (nq < nk),
+    from row-strided views of one fused QKV buffer, vs torch per sequence."""
+    for gi, (_, H_q, H_kv, d) in enumerate(GEOMS):
+        specs = [(0, 7), (16, 5), (35, 18), (5, 1), (0, 33), (0, 0)]  # (prefix, new)
+        g = torch.Generator().manual_seed(40 + gi)
+        nq = [n for _, n in specs]
+        nk = [c + n for c, n in specs]
+        cu_q = [0]
+        cu_k = [0]
+        for a, b in zip(nq, nk):
+            cu_q.append(cu_q[-1] + a)
+            cu_k.append(cu_k[-1] + b)
+        # fused rows: q of the new tokens and k/v of all keys, one buffer each
+        width = (H_q + 2 * H_kv) * d
+        qbuf = torch.randn(cu_q[-1], width, generator=g).to(torch.bfloat16)
+        kvbuf = torch.randn(cu_k[-1], width, generator=g).to(torch.bfloat16)
+        q = qbuf[:, : H_q * d].view(-1, H_q, d)
+        k = kvbuf[:, H_q * d: (H_q + H_kv) * d].view(-1, H_kv, d)
+        v = kvbuf[:, (H_q + H_kv) * d:].view(-1, H_kv, d)
+        scale = 1.0 / math.sqrt(d)
+        out = orc.prefill_packed(q, k, v, cu_q, cu_k, scale)
+        assert torch.isfinite(out).all()
+        for b in range(len(specs)):
+            if nq[b] == 0:
+                continue
+            mask = causal_lower_right(nq[b], nk[b])
+            ref = _sdpa(q[cu_q[b]:cu_q[b + 1]], k[cu_k[b]:cu_k[b + 1]].double(),
+                        v[cu_k[b]:cu_k[b + 1]].double(),
+                        float(torch.tensor(scale, dtype=torch.float32)), mask)
+            err = (out[cu_q[b]:cu_q[b + 1]] - ref).abs().max().item()
+            assert err < TOL, f"packed prefill vs library: seq {b} geom {gi} err {err}"
+
+
 ATTENTION_PINS = [
     pin_decode_equals_library,
     pin_prefill_equals_library,
@@ -263,4 +298,5 @@ ATTENTION_PINS = [
     pin_prefill_one_equals_decode,
     pin_chunked_prefill,
     pin_shared_prefix,
+    pin_packed_prefill_equals_library,
 ]

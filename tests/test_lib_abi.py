@@ -94,6 +94,27 @@ def test_attention_argument_checks_before_launch():
                                   None) == 0  # nothing to do
 
 
+def test_packed_prefill_argument_checks_before_launch():
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(4096 + 16)
+    p = (ctypes.addressof(buf) + 15) // 16 * 16
+
+    def pk(qs=512, ks=256, vs=256, B=2, tq=10, tk=10, mq=10, H_q=8, H_kv=4, d=64, q=p):
+        return lib.pkv_prefill_varlen_packed(p, q, qs, p, ks, p, vs, p, p, B, tq, tk, mq, mq,
+                                             H_q, H_kv, d, 0.125, None)
+
+    assert pk(B=0) == 0 and pk(tq=0) == 0 and pk(mq=0) == 0   # nothing to do
+    assert pk(qs=256) == 1        # q stride below H_q * d
+    assert pk(ks=250) == 1        # not a multiple of 8, below the row
+    assert pk(vs=260) == 1        # not a multiple of 8
+    assert pk(H_q=6) == 1         # H_q % H_kv
+    assert pk(q=p + 2) == 1       # misaligned
+    assert pk(tk=0) == 1          # no keys
+    assert pk(B=-1) == 1
+    assert pk(d=96, qs=768, ks=384, vs=384) == 2
+    assert pk(H_q=64, H_kv=4, qs=4096) == 2  # group of 16
+
+
 def test_workspace_size_formula():
     lib = _lib.load()
     # partial slots per share of the schedule, plus 16 bytes per (sequence, KV head)
