@@ -229,6 +229,69 @@ def run_packed(steps, warmup, torch, pkv, log):
                 tokens_per_s=round(sum(lens) / (ms * 1e-3), 1), flops=fl)
 
 
+def run_graph(steps, warmup, torch, pkv, log):
+    """28-layer decode step (store + decode per layer) at small batches, three
+    ways: eager calls from Python, the same launches issued by the library
+    (pkv_decode_step_run), and the bucketed graph replay (pkv_decode_graph_replay,
+    which pads to the bucket).  Wall time per step over `steps` back-to-back
+    steps, synchronised at both ends."""
+    from workloads import make_tensors
+    from workloads.graph import GRAPH_DECODE as cfg, graph_plan
+
+    plan = graph_plan()
+    L, mb = cfg["layers"], cfg["max_batch"]
+    tens = make_tensors(plan, "cuda", poison=False)
+    meta = pkv.prepare_metadata(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    dm = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in meta.items()}
+    graph = pkv.DecodeGraph([tens.k_cache(l) for l in range(L)], [tens.v_cache(l) for l in range(L)],
+                            mb, plan.H_q, plan.max_blocks_per_seq)
+    scale = 1.0 / math.sqrt(plan.d)
+    ws = torch.zeros(pkv.decode_workspace_size(mb, plan.H_q, plan.H_kv, plan.d, plan.block_size,
+                                               plan.max_blocks_per_seq),
+                     dtype=torch.uint8, device="cuda")
+    res = dict(workload="graph_decode", layers=L, H_q=plan.H_q, H_kv=plan.H_kv, d=plan.d,
+               block_size=plan.block_size, context=list(cfg["context"]), batches={})
+    for batch in cfg["batches"]:
+        graph.slot_mapping[:batch].copy_(dm["slot_mapping"][:batch])
+        graph.context_lens[:batch].copy_(dm["context_lens"][:batch])
+        graph.block_tables[:batch].copy_(dm["block_tables"][:batch])
+        graph.q[:, :batch].copy_(tens.q[:, :batch])
+        graph.kv_new[:, :batch].copy_(tens.kv_new[:, :batch])
+        sl, cl, bt = (dm["slot_mapping"][:batch], dm["context_lens"][:batch],
+                      dm["block_tables"][:batch])
+        outs = [torch.empty_like(tens.q[l][:batch]) for l in range(L)]
+
+        def eager_py():
+            for l in range(L):
+                kc, vc = tens.k_cache(l), tens.v_cache(l)
+                pkv.store(tens.k_new(l)[:batch], tens.v_new(l)[:batch], kc, vc, sl)
+                pkv.decode(tens.q[l][:batch], kc, vc, bt, cl, scale, out=outs[l], workspace=ws)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / steps
+
+        row = dict(bucket=graph.bucket(batch),
+                   eager_python_ms=round(timed(eager_py), 4),
+                   eager_native_ms=round(timed(lambda: graph.run_eager(batch)), 4),
+                   graph_ms=round(timed(lambda: graph.replay(batch)), 4))
+        kv = sum(2 * s.total * plan.H_kv * plan.d * 2 for s in plan.seqs[:batch]) * L
+        row["graph_kv_gb_per_s"] = round(kv / (row["graph_ms"] * 1e-3) / 1e9, 2)
+        row["speedup_vs_eager_python"] = round(row["eager_python_ms"] / row["graph_ms"], 3)
+        res["batches"][str(batch)] = row
+        log(f"graph_decode batch {batch}: {json.dumps(row)}")
+    graph.close()
+    del tens, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
     """Plain device copy (torch copy_) and plain read (torch sum) of a buffer of known
     size: the achievable-bandwidth reference for the roofline, and the known-size
@@ -321,6 +384,7 @@ def main() -> int:
     if not args.no_secondary:
         secondary["packed_prefill"] = run_packed(max(5, args.steps // 2), 2, torch, pkv, log)
         log(json.dumps(secondary["packed_prefill"]))
+        secondary["graph_decode"] = run_graph(max(5, args.steps // 2), 3, torch, pkv, log)
         for name in ["long_decode", "prefix_prefill", "full_step"]:
             if name == args.workload:
                 continue

@@ -119,8 +119,8 @@ pkv_status pkv_store(const void* key, int64_t key_stride, const void* value,
 /*
  * Bytes of device workspace pkv_decode needs for these sizes on the current
  * HIP device: two fp32 partial results (max, sum, d-vector) per query head of
- * a group for every share of the work schedule (8 shares per resident
- * wavefront of the device), a 16-byte record per (sequence, KV head), and a
+ * a group for every share of the work schedule (2W + 14*ceil(W/2) shares
+ * for the W resident wavefronts of the device), a 16-byte record per (sequence, KV head), and a
  * 256-byte line holding the schedule's share counter.  Query it with the
  * device current that will run the decode.  0 for invalid or unsupported
  * sizes.
@@ -231,6 +231,110 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
                                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t H_q,
                                      int32_t H_kv, int32_t d, float softmax_scale,
                                      hipStream_t stream);
+
+/*
+ * Graph-captured decode step with batch buckets (devpress page,
+ * "CUDAGraph优化"; AIInfraGuide 3.6, section 5).  A decode step is, for every
+ * layer l, pkv_store of the batch's new K/V rows into layer l's caches
+ * followed by pkv_decode over them.  Its kernels, launch shapes and their
+ * order depend only on the batch size, so one graph is captured per batch
+ * bucket over static buffers sized for max_batch rows, and a step of `batch`
+ * rows replays the smallest bucket >= batch with the rows beyond `batch`
+ * padded: slot -1 (the store skips them) and context length 0 (their outputs
+ * are zero rows).
+ *
+ * Buckets: 1, 2, 4, 8, then every multiple of 16 up to max_batch, then
+ * max_batch itself when it is not already one (the pages' list stops at the
+ * last multiple of 16; adding max_batch lets every batch up to it replay).
+ * Batches above max_batch (above 512 in the pages) run eagerly: the caller
+ * issues pkv_store / pkv_decode itself.
+ */
+typedef struct pkv_decode_graph pkv_decode_graph;
+
+/*
+ * The step a graph set captures.  All pointers are device pointers except
+ * the per-layer arrays themselves (host arrays of `layers` device pointers,
+ * read at create time; the graphs bake in the device addresses, so the
+ * buffers must stay allocated and in place while the graph set exists).
+ *   slot_mapping   [max_batch] int32   rows [0, batch) written by the caller
+ *   context_lens   [max_batch] int32   before each replay; the replay writes
+ *                                      the padding rows [batch, bucket)
+ *   block_tables   [max_batch, max_blocks_per_seq] int32
+ *   q[l], out[l]   [max_batch, H_q, d] bf16, contiguous
+ *   key[l], value[l]   [max_batch, H_kv, d] bf16 rows key_stride /
+ *                  value_stride elements apart (as for pkv_store)
+ *   k_cache[l], v_cache[l]   [num_blocks, block_size, H_kv, d] bf16
+ *   workspace      pkv_decode_workspace_size(max_batch, ...) bytes or more,
+ *                  zero-filled before create, used by nothing else while
+ *                  the graph set exists (every layer of every replay uses it
+ *                  in stream order).
+ */
+typedef struct pkv_decode_step {
+  int32_t layers;
+  int32_t max_batch;
+  int32_t H_q, H_kv, d;
+  int32_t num_blocks, block_size, max_blocks_per_seq;
+  float softmax_scale;
+  int32_t* slot_mapping;
+  int32_t* context_lens;
+  const int32_t* block_tables;
+  const void* const* q;
+  const void* const* key;
+  const void* const* value;
+  int64_t key_stride, value_stride;
+  void* const* k_cache;
+  void* const* v_cache;
+  void* const* out;
+  void* workspace;
+  size_t workspace_bytes;
+} pkv_decode_step;
+
+/*
+ * Bucket a batch of `batch` rows replays for a graph set of max_batch rows:
+ * the smallest bucket >= batch; -1 when batch < 1, batch > max_batch or
+ * max_batch is outside [1, 512].  Host only.
+ */
+int32_t pkv_decode_graph_bucket(int32_t max_batch, int32_t batch);
+
+/*
+ * Captures one graph per bucket on the current HIP device.  Blocking set-up
+ * call: it first writes slot -1 and context length 0 to all max_batch rows,
+ * runs the step once eagerly on those all-padding rows (which loads every
+ * kernel and writes zero rows to out[*][0, max_batch)), captures the graphs
+ * on a stream of its own and waits for that stream.  On success *graph owns
+ * the graphs; release them with pkv_decode_graph_destroy.
+ * PKV_EINVAL: null pointers, layers < 1, max_batch outside [1, 512], a
+ * workspace smaller than needed, or any argument pkv_store / pkv_decode
+ * would reject.  PKV_EUNSUPPORTED as for pkv_decode.  PKV_ELAUNCH: the HIP
+ * runtime failed (nothing is left allocated).
+ */
+pkv_status pkv_decode_graph_create(const pkv_decode_step* step, pkv_decode_graph** graph);
+
+/*
+ * Enqueues one decode step of `batch` rows on `stream`: a small kernel that
+ * writes slot -1 and context length 0 to rows [batch, bucket) (none when
+ * batch is a bucket), then the bucket's graph.  The caller has written rows
+ * [0, batch) of the static metadata, q, key and value, in stream order.
+ * Afterwards out[l] rows [0, batch) hold the attention outputs, rows
+ * [batch, bucket) are zero, rows beyond the bucket are untouched.  Replays
+ * of one graph set share its workspace: they must be ordered (one stream, or
+ * events).  batch == 0 enqueues nothing.
+ * PKV_EINVAL: null graph, batch < 0 or batch > max_batch.  PKV_ELAUNCH: the
+ * HIP runtime failed.
+ */
+pkv_status pkv_decode_graph_replay(pkv_decode_graph* graph, int32_t batch, hipStream_t stream);
+
+/*
+ * The same step issued eagerly on `stream` (the pages' enforce_eager branch):
+ * for each layer, pkv_store and pkv_decode over rows [0, batch) of the
+ * step's buffers, with no padding.  Not blocking.  Same errors as
+ * pkv_decode_graph_create for the step, plus batch outside [0, max_batch].
+ */
+pkv_status pkv_decode_step_run(const pkv_decode_step* step, int32_t batch, hipStream_t stream);
+
+/* Waits for the device to finish all enqueued work (so no replay is still
+ * running), then releases the graphs.  Null is a no-op. */
+void pkv_decode_graph_destroy(pkv_decode_graph* graph);
 
 #ifdef __cplusplus
 }

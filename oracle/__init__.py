@@ -3,7 +3,8 @@
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product library never loads it and shares no code
 with it: the C part (``pkv_oracle.c``) is compiled by gcc into its own shared
-object, and the metadata loops live in ``metadata.py``.
+object, the metadata loops live in ``metadata.py`` and the decode-graph bucket
+rule in ``graph.py``.
 
 Inputs are CPU torch tensors (bf16 data is passed as its raw 16-bit patterns);
 attention outputs come back as float64 tensors.
@@ -18,6 +19,7 @@ from typing import Optional
 import numpy as np
 import torch
 
+from . import graph
 from .metadata import prepare_decode, prepare_prefill
 
 HERE = os.path.dirname(os.path.abspath(__file__))

@@ -13,6 +13,9 @@ Functions:
     decode(q, k_cache, v_cache, block_tables, context_lens, softmax_scale=None, ...)
     prefill_varlen(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
                    max_seqlen_q, max_seqlen_k, softmax_scale=None, ...)
+    prefill_varlen_packed(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
+    graph_bucket(max_batch, batch) -> int
+    DecodeGraph(k_caches, v_caches, max_batch, H_q, max_blocks_per_seq, ...)
 """
 from __future__ import annotations
 
@@ -22,11 +25,12 @@ from typing import Optional, Sequence
 
 import torch
 
-from ._lib import EXPORTS, LIB_PATH, PkvError, check, load
+from ._lib import EXPORTS, LIB_PATH, DecodeStep, PkvError, check, load
 
 __all__ = [
     "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
-    "prefill_varlen_packed", "PkvError", "LIB_PATH", "EXPORTS", "version",
+    "prefill_varlen_packed", "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
+    "version",
 ]
 
 
@@ -215,3 +219,93 @@ def prefill_varlen_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, total_q, total_k, int(max_seqlen_q),
         int(max_seqlen_k), H_q, H_kv, d, scale, _stream(stream)))
     return out
+
+
+def graph_bucket(max_batch: int, batch: int) -> int:
+    """Bucket a batch of ``batch`` rows replays in a graph set of ``max_batch``
+    rows (-1 when there is none)."""
+    return int(load().pkv_decode_graph_bucket(int(max_batch), int(batch)))
+
+
+class DecodeGraph:
+    """Graph-captured decode step with batch buckets (pkv_decode_graph_* in
+    include/pkv.h): every layer's store + decode, one HIP graph per bucket.
+
+    The static buffers, sized for ``max_batch`` rows, are allocated here with
+    torch and filled by the caller before each step (rows ``[0, batch)``):
+    ``slot_mapping``, ``context_lens``, ``block_tables``, ``q[l]``, ``key[l]``,
+    ``value[l]`` (views of one fused ``kv_new[l]`` buffer, K then V per token).
+    After ``replay(batch)`` (or ``run_eager(batch)``), ``out[l][:batch]`` holds
+    layer l's attention output.  ``k_caches`` / ``v_caches`` are the per-layer
+    cache tensors ``[num_blocks, block_size, H_kv, d]``; they must outlive the
+    graphs.  Batches above ``max_batch`` are the caller's eager calls.
+    """
+
+    def __init__(self, k_caches, v_caches, max_batch: int, H_q: int, max_blocks_per_seq: int,
+                 softmax_scale: Optional[float] = None):
+        _need(len(k_caches) == len(v_caches) and len(k_caches) >= 1, "one k and v cache per layer")
+        geo = _cache_geometry(k_caches[0], v_caches[0])
+        for kc, vc in zip(k_caches, v_caches):
+            _need(_cache_geometry(kc, vc) == geo, "every layer's caches must have one geometry")
+        nb, bs, H_kv, d = geo
+        L, dev = len(k_caches), k_caches[0].device
+        self.layers, self.max_batch = L, int(max_batch)
+        self.H_q, self.H_kv, self.d = int(H_q), H_kv, d
+        self.k_caches, self.v_caches = list(k_caches), list(v_caches)
+        mb = self.max_batch
+        self.slot_mapping = torch.full((mb,), -1, dtype=torch.int32, device=dev)
+        self.context_lens = torch.zeros(mb, dtype=torch.int32, device=dev)
+        self.block_tables = torch.full((mb, max_blocks_per_seq), -1, dtype=torch.int32, device=dev)
+        self.q = torch.zeros((L, mb, H_q, d), dtype=torch.bfloat16, device=dev)
+        self.kv_new = torch.zeros((L, mb, 2 * H_kv * d), dtype=torch.bfloat16, device=dev)
+        self.key = [self.kv_new[l, :, : H_kv * d].view(mb, H_kv, d) for l in range(L)]
+        self.value = [self.kv_new[l, :, H_kv * d:].view(mb, H_kv, d) for l in range(L)]
+        self.out = torch.zeros((L, mb, H_q, d), dtype=torch.bfloat16, device=dev)
+        ws = decode_workspace_size(mb, H_q, H_kv, d, bs, max_blocks_per_seq)
+        _need(ws > 0, "unsupported decode shape")
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
+        arr = ctypes.c_void_p * L
+        self._arrays = [
+            arr(*[self.q[l].data_ptr() for l in range(L)]),
+            arr(*[t.data_ptr() for t in self.key]),
+            arr(*[t.data_ptr() for t in self.value]),
+            arr(*[t.data_ptr() for t in self.k_caches]),
+            arr(*[t.data_ptr() for t in self.v_caches]),
+            arr(*[self.out[l].data_ptr() for l in range(L)]),
+        ]
+        aq, ak, av, akc, avc, ao = self._arrays
+        scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+        self._step = DecodeStep(
+            L, mb, self.H_q, H_kv, d, nb, bs, int(max_blocks_per_seq), scale,
+            self.slot_mapping.data_ptr(), self.context_lens.data_ptr(),
+            self.block_tables.data_ptr(), aq, ak, av, self.kv_new.stride(1),
+            self.kv_new.stride(1), akc, avc, ao, self.workspace.data_ptr(), ws)
+        handle = ctypes.c_void_p(0)
+        check("pkv_decode_graph_create",
+              load().pkv_decode_graph_create(ctypes.byref(self._step), ctypes.byref(handle)))
+        self._handle = handle
+
+    def bucket(self, batch: int) -> int:
+        return graph_bucket(self.max_batch, batch)
+
+    def replay(self, batch: int, stream=None) -> None:
+        """Pads rows [batch, bucket) and replays the bucket's graph."""
+        _need(self._handle is not None, "graphs already released")
+        check("pkv_decode_graph_replay",
+              load().pkv_decode_graph_replay(self._handle, int(batch), _stream(stream)))
+
+    def run_eager(self, batch: int, stream=None) -> None:
+        """The same step as individual launches over rows [0, batch)."""
+        check("pkv_decode_step_run",
+              load().pkv_decode_step_run(ctypes.byref(self._step), int(batch), _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None:
+            load().pkv_decode_graph_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -23,7 +23,30 @@ EXPORTS = (
     "pkv_decode",
     "pkv_prefill_varlen",
     "pkv_prefill_varlen_packed",
+    "pkv_decode_graph_bucket",
+    "pkv_decode_graph_create",
+    "pkv_decode_graph_replay",
+    "pkv_decode_step_run",
+    "pkv_decode_graph_destroy",
 )
+
+
+class DecodeStep(ctypes.Structure):
+    """Mirror of pkv_decode_step (include/pkv.h)."""
+    _fields_ = [
+        ("layers", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+        ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("slot_mapping", ctypes.c_void_p), ("context_lens", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("q", ctypes.POINTER(ctypes.c_void_p)), ("key", ctypes.POINTER(ctypes.c_void_p)),
+        ("value", ctypes.POINTER(ctypes.c_void_p)),
+        ("key_stride", ctypes.c_int64), ("value_stride", ctypes.c_int64),
+        ("k_cache", ctypes.POINTER(ctypes.c_void_p)), ("v_cache", ctypes.POINTER(ctypes.c_void_p)),
+        ("out", ctypes.POINTER(ctypes.c_void_p)),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
 
 
 class PkvError(RuntimeError):
@@ -65,6 +88,17 @@ def load() -> ctypes.CDLL:
     lib.pkv_prefill_varlen_packed.argtypes = [P, P, I64, P, I64, P, I64, P, P, I32, I32, I32, I32,
                                               I32, I32, I32, I32, F, P]
     lib.pkv_prefill_varlen_packed.restype = ctypes.c_int
+    SP = ctypes.POINTER(DecodeStep)
+    lib.pkv_decode_graph_bucket.argtypes = [I32, I32]
+    lib.pkv_decode_graph_bucket.restype = I32
+    lib.pkv_decode_graph_create.argtypes = [SP, ctypes.POINTER(P)]
+    lib.pkv_decode_graph_create.restype = ctypes.c_int
+    lib.pkv_decode_graph_replay.argtypes = [P, I32, P]
+    lib.pkv_decode_graph_replay.restype = ctypes.c_int
+    lib.pkv_decode_step_run.argtypes = [SP, I32, P]
+    lib.pkv_decode_step_run.restype = ctypes.c_int
+    lib.pkv_decode_graph_destroy.argtypes = [P]
+    lib.pkv_decode_graph_destroy.restype = None
     _lib = lib
     return lib
 

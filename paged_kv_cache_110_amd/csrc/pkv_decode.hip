@@ -706,7 +706,7 @@ struct WaveQuery {
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace: two fp32 partial slots (acc[d], then (m, l)) per query head of
-// a group for every share of the schedule (kLevels * W shares), one SegInfo
+// a group for every share the schedule can hold (ShareSchedule::max_shares), one SegInfo
 // per (sequence, KV head), and the share counter in its own 256-byte line.
 struct WorkspaceLayout {
   size_t acc, ml, seg, queue, total;

@@ -13,10 +13,15 @@ hipError_t launch_store(const uint16_t* key, int64_t key_stride, const uint16_t*
                         const int32_t* slot_mapping, int32_t num_tokens, int64_t num_slots,
                         int32_t row_elems, hipStream_t stream);
 
+// Rows [from, to) of a bucketed decode step's metadata become padding:
+// slot_mapping -1, context_lens 0.
+hipError_t launch_pad_batch(int32_t* slot_mapping, int32_t* context_lens, int32_t from,
+                            int32_t to, hipStream_t stream);
+
 // Decode launch plan: one wavefront per resident slot of the current device.
 struct DecodePlan {
   int32_t num_waves;       // 0 when the shape has no kernel
-  size_t workspace_bytes;  // two partial slots per wavefront + one record per (sequence, KV head)
+  size_t workspace_bytes;  // partial slots per share + one record per (sequence, KV head)
 };
 DecodePlan decode_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t d, int32_t block_size,
                        int32_t max_blocks_per_seq);

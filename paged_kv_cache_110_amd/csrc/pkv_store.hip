@@ -43,4 +43,24 @@ hipError_t launch_store(const uint16_t* key, int64_t key_stride, const uint16_t*
   return hipGetLastError();
 }
 
+// Padding rows of a bucketed decode step: slot -1 (the store skips the row)
+// and context length 0 (the decode writes a zero row).
+__global__ __launch_bounds__(256) void pad_batch_kernel(int32_t* __restrict__ slot_mapping,
+                                                        int32_t* __restrict__ context_lens,
+                                                        int32_t from, int32_t to) {
+  const int32_t i = from + (int32_t)(blockIdx.x * 256 + threadIdx.x);
+  if (i >= to) return;
+  slot_mapping[i] = -1;
+  context_lens[i] = 0;
+}
+
+hipError_t launch_pad_batch(int32_t* slot_mapping, int32_t* context_lens, int32_t from,
+                            int32_t to, hipStream_t stream) {
+  if (to <= from) return hipSuccess;
+  const unsigned blocks = (unsigned)((to - from + 255) / 256);
+  hipLaunchKernelGGL(pad_batch_kernel, dim3(blocks), dim3(256), 0, stream, slot_mapping,
+                     context_lens, from, to);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -300,3 +300,55 @@ ATTENTION_PINS = [
     pin_shared_prefix,
     pin_packed_prefill_equals_library,
 ]
+
+
+# ------------------------------------------------------------ decode-graph buckets
+
+def _graph_fixture():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "graph_buckets.json")
+    with open(path) as f:
+        return json.load(f)
+
+
+def pin_graph_bucket_list(g):
+    """The preset list for a largest batch of 512, as the pages' formula gives it."""
+    fx = _graph_fixture()
+    b = g.buckets(fx["max_batch"])
+    assert len(b) == fx["count"], f"{len(b)} buckets for 512, want {fx['count']}"
+    assert b[:len(fx["first"])] == fx["first"], b[:8]
+    assert b[-len(fx["last"]):] == fx["last"], b[-3:]
+    assert g.buckets(0) == [] and g.buckets(513) == []
+
+
+def pin_graph_bucket_choice(g):
+    """The chosen bucket is the smallest listed size not below the batch;
+    batches above the largest run eagerly."""
+    fx = _graph_fixture()
+    for batch, want in fx["choices"]:
+        got = g.bucket_for(fx["max_batch"], batch)
+        assert got == want, f"batch {batch}: bucket {got}, want {want}"
+    for batch in fx["eager"] + [0, -1]:
+        assert g.bucket_for(fx["max_batch"], batch) == -1, batch
+    # small largest batches: the list holds exactly the powers 1..8 and the
+    # multiples of 16 up to it, plus the largest batch itself
+    for mb in (1, 2, 3, 5, 8, 9, 15, 16, 17, 40, 100):
+        want = sorted({x for x in (1, 2, 4, 8) if x <= mb} | set(range(16, mb + 1, 16)) | {mb})
+        assert g.buckets(mb) == want, (mb, g.buckets(mb))
+        for batch in range(1, mb + 1):
+            got = g.bucket_for(mb, batch)
+            assert got >= batch and got in want, (mb, batch, got)
+            assert not [x for x in want if batch <= x < got], (mb, batch, got)
+
+
+def pin_graph_padding(g):
+    """Rows past the batch become padding: slot -1 (not stored), length 0."""
+    slots, lens = g.pad_rows([40, 7, 1029], [41, 8, 1030], 3, 8)
+    assert slots == [40, 7, 1029, -1, -1, -1, -1, -1], slots
+    assert lens == [41, 8, 1030, 0, 0, 0, 0, 0], lens
+    slots, lens = g.pad_rows([3, 4], [5, 6], 2, 2)
+    assert (slots, lens) == ([3, 4], [5, 6])
+
+
+GRAPH_PINS = [pin_graph_bucket_list, pin_graph_bucket_choice, pin_graph_padding]

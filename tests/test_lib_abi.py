@@ -180,3 +180,50 @@ def test_prepare_metadata_random_plans():
         got = pkv.prepare_metadata(plan.seqs, bs, plan.max_blocks_per_seq + trial % 2)
         ref = O.prepare_prefill(plan.seqs, bs, plan.max_blocks_per_seq + trial % 2)
         _meta_equal(got, ref)
+
+
+# ------------------------------------------------------------ decode-graph step
+
+
+def test_graph_bucket_matches_oracle():
+    lib = _lib.load()
+    for mb in (1, 2, 3, 7, 8, 9, 16, 17, 40, 100, 511, 512, 0, 513, -4):
+        for batch in list(range(-1, min(mb, 70) + 3)) + [mb - 1, mb, mb + 1, 1000]:
+            assert lib.pkv_decode_graph_bucket(mb, batch) == O.graph.bucket_for(mb, batch), (mb, batch)
+
+
+def test_step_struct_layout_matches_c(tmp_path):
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    exe = str(tmp_path / "step_layout")
+    subprocess.run([gcc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(rocm, "include"),
+                    os.path.join(ROOT, "tests", "native", "step_layout.c"), "-o", exe], check=True)
+    lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = dict(line.split() for line in lines if line.strip())
+    assert int(got.pop("size")) == ctypes.sizeof(_lib.DecodeStep)
+    for name, off in got.items():
+        assert getattr(_lib.DecodeStep, name).offset == int(off), name
+    assert len(got) == len(_lib.DecodeStep._fields_)
+
+
+def test_graph_argument_checks_before_any_hip_call():
+    lib = _lib.load()
+    handle = ctypes.c_void_p(0)
+    assert lib.pkv_decode_graph_create(None, ctypes.byref(handle)) == 1
+    step = _lib.DecodeStep()
+    assert lib.pkv_decode_graph_create(ctypes.byref(step), None) == 1
+    assert lib.pkv_decode_graph_create(ctypes.byref(step), ctypes.byref(handle)) == 1  # layers 0
+    step.layers, step.max_batch = 1, 513  # above the graph limit
+    assert lib.pkv_decode_graph_create(ctypes.byref(step), ctypes.byref(handle)) == 1
+    step.max_batch = 8  # null buffers
+    assert lib.pkv_decode_graph_create(ctypes.byref(step), ctypes.byref(handle)) == 1
+    assert handle.value is None
+    assert lib.pkv_decode_graph_replay(None, 1, None) == 1
+    assert lib.pkv_decode_step_run(None, 1, None) == 1
+    assert lib.pkv_decode_step_run(ctypes.byref(step), 1, None) == 1
+    lib.pkv_decode_graph_destroy(None)  # no-op

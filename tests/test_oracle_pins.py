@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from pins import ATTENTION_PINS
+from pins import ATTENTION_PINS, GRAPH_PINS
 from workloads import SeqState, custom_plan, make_plan, make_tensors, NAN_BF16_BITS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -211,3 +211,11 @@ def test_poisoned_tiny_config_is_finite(orc):
     G = plan.H_q // plan.H_kv
     for h in range(plan.H_q):
         assert torch.equal(out[0, h], tens.v_new()[0, h // G].double())
+
+
+# ------------------------------------------------------------ decode-graph buckets
+
+
+@pytest.mark.parametrize("pin", GRAPH_PINS, ids=lambda p: p.__name__)
+def test_graph_bucket_oracle(pin):
+    pin(O.graph)

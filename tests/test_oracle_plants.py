@@ -3,10 +3,12 @@
 The oracle source compiles one deliberate error when built with
 -DPKV_ORACLE_PLANT=n; the default build has none.
 """
+import types
+
 import pytest
 
 import oracle as O
-from pins import ATTENTION_PINS
+from pins import ATTENTION_PINS, GRAPH_PINS
 
 PLANTS = {
     1: "drops the newest key",
@@ -32,3 +34,50 @@ def test_plant_is_caught(plant):
 
 def test_clean_build_has_no_plant():
     assert O.Oracle(0).lib.pkv_oracle_plant() == 0
+
+
+# Planted mistakes in the decode-graph bucket rule (oracle/graph.py), each a
+# plausible misreading of the pages' list or of the padding.
+def _stop_short(mb):  # the list's end taken as exclusive
+    return [b for b in (1, 2, 4, 8) if b <= mb] + list(range(16, mb, 16))
+
+
+def _strict_choice(mb, batch):
+    return next((b for b in O.graph.buckets(mb) if b > batch), -1) if batch >= 1 else -1
+
+
+def _powers_of_two(mb):
+    out, b = [], 1
+    while b <= mb:
+        out.append(b)
+        b *= 2
+    return out if out and out[-1] == mb else out + [mb]
+
+
+def _pad_with_zero_slot(slots, lens, batch, bucket):
+    return list(slots[:batch]) + [0] * (bucket - batch), list(lens[:batch]) + [0] * (bucket - batch)
+
+
+GRAPH_PLANTS = {
+    "list_stops_before_the_largest_batch": dict(buckets=_stop_short),
+    "strictly_larger_bucket": dict(bucket_for=_strict_choice),
+    "powers_of_two_only": dict(buckets=_powers_of_two,
+                               bucket_for=lambda mb, b: next(
+                                   (x for x in _powers_of_two(mb) if x >= b), -1) if b >= 1 else -1),
+    "padding_slot_zero": dict(pad_rows=_pad_with_zero_slot),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GRAPH_PLANTS))
+def test_graph_plant_is_caught(name):
+    planted = types.SimpleNamespace(buckets=O.graph.buckets, bucket_for=O.graph.bucket_for,
+                                    pad_rows=O.graph.pad_rows)
+    for k, fn in GRAPH_PLANTS[name].items():
+        setattr(planted, k, fn)
+    caught = []
+    for pin in GRAPH_PINS:
+        try:
+            pin(planted)
+        except AssertionError as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, f"planted mistake '{name}' passed every pin"
