@@ -3,6 +3,11 @@
 // for W wavefronts.  Plain C++ usable on the host and the device, so the
 // layout can be checked on the CPU.
 //
+// A call of at most kMinStaticUnits units per wavefront is one static pass
+// of ceil(T / W) units per wavefront, but at least PKV_SCHED_SMALL_MIN, so
+// that more wavefronts start at once (small batches are latency-bound) while
+// segments are not cut into more pieces than the merge gathers quickly.
+// Larger calls:
 // Level 0: one static share of S0 units per wavefront, about 40% of the
 // work, ending at unit P1.  Levels 1..kLevels-2 hold N = ceil(W / 2) shares
 // each and are handed out in order through an atomic counter: level 1's
@@ -34,6 +39,9 @@ struct ShareSchedule {
 #ifndef PKV_SCHED_DYN_MIN
 #define PKV_SCHED_DYN_MIN 16
 #endif
+#ifndef PKV_SCHED_SMALL_MIN
+#define PKV_SCHED_SMALL_MIN 4  // least units per wavefront in a one-pass call
+#endif
 #ifndef PKV_SCHED_SHRINK
 #define PKV_SCHED_SHRINK 2  // each level keeps 1 - 2^-SHRINK of the previous size
 #endif
@@ -48,8 +56,13 @@ struct ShareSchedule {
     ShareSchedule s;
     s.T = T;
     s.W = W;
-    const int s0 = (int)(((int64_t)T * PKV_SCHED_STATIC_NUM / PKV_SCHED_STATIC_DEN) / W);
-    s.S0 = s0 < kMinStaticUnits ? kMinStaticUnits : s0;
+    const int64_t per_wave = ((int64_t)T + W - 1) / W;
+    if (per_wave <= kMinStaticUnits) {
+      s.S0 = per_wave < PKV_SCHED_SMALL_MIN ? PKV_SCHED_SMALL_MIN : (int)per_wave;
+    } else {
+      const int s0 = (int)(((int64_t)T * PKV_SCHED_STATIC_NUM / PKV_SCHED_STATIC_DEN) / W);
+      s.S0 = s0 < kMinStaticUnits ? kMinStaticUnits : s0;
+    }
     s.P1 = (int64_t)s.S0 * W < T ? s.S0 * W : T;
     s.N = (W + 1) / 2;
     const int s1 = (int)(((int64_t)(T - s.P1) + 2 * (int64_t)W - 1) / (2 * (int64_t)W));

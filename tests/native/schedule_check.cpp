@@ -8,7 +8,9 @@
 //      and when dynamic shares exist every static share is non-empty;
 //   5. no more than max_shares(W) shares; dynamic shares shrink (never grow)
 //      from one level to the next, except for the last level (W shares that
-//      split whatever remains).
+//      split whatever remains);
+//   6. a call of at most kMinStaticUnits units per wavefront is static and
+//      gives no wavefront more than max(ceil(T / W), PKV_SCHED_SMALL_MIN) units.
 #include <cstdio>
 #include <cstdint>
 
@@ -57,6 +59,16 @@ static int check(int T, int W) {
     next = en;
   }
   if (next != T) return fail("coverage", T, W, next, 0);
+  const long long per_wave = ((long long)T + W - 1) / W;
+  if (per_wave <= pkv::ShareSchedule::kMinStaticUnits) {
+    if (s.dynamic()) return fail("small call not static", T, W, per_wave, 0);
+    for (int k = 0; k < W; ++k) {
+      int st = 0, en = 0;
+      s.range(k, st, en);
+      const long long cap = per_wave > PKV_SCHED_SMALL_MIN ? per_wave : PKV_SCHED_SMALL_MIN;
+      if (en - st > cap) return fail("small call share size", T, W, k, en - st);
+    }
+  }
   if (s.dynamic()) {
     for (int k = 0; k < W; ++k) {
       int st = 0, en = 0;
