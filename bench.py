@@ -292,6 +292,53 @@ def run_graph(steps, warmup, torch, pkv, log):
     return res
 
 
+def run_meta(steps, warmup, torch, pkv, log):
+    """Step metadata two ways on the decode and prefill workloads: the host
+    routine (pkv_prepare_metadata through the binding) plus pinned copies to the
+    device, against one kernel (pkv_prepare_metadata_device) that derives it
+    from request state kept on the device.  Wall time per step, synchronised;
+    the device call's figure is the binding's per-call host time, since the
+    kernel itself is shorter."""
+    from workloads import make_plan
+
+    res = {}
+    for name in ("qwen3_decode", "prefix_prefill"):
+        plan = make_plan(name)
+        bs, maxb, B = plan.block_size, plan.max_blocks_per_seq, plan.B
+        hm = pkv.prepare_metadata(plan.seqs, bs, maxb)
+        table = hm["block_tables"].to("cuda")
+        computed = torch.tensor([s.num_cached for s in plan.seqs], dtype=torch.int32, device="cuda")
+        sched = torch.tensor([s.num_new for s in plan.seqs], dtype=torch.int32, device="cuda")
+        total = plan.total_new
+        bufs = pkv.prepare_metadata_device(None, computed, sched, table, bs, maxb, total)
+
+        def host():
+            m = pkv.prepare_metadata(plan.seqs, bs, maxb)
+            for k in ("slot_mapping", "context_lens", "cu_seqlens_q", "cu_seqlens_k", "block_tables"):
+                m[k].pin_memory().to("cuda", non_blocking=True)
+
+        def device():
+            pkv.prepare_metadata_device(None, computed, sched, table, bs, maxb, total, out=bufs)
+
+        def wall(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / steps
+
+        out_bytes = 4 * (2 * (B + 1) + B + total + B * maxb + 2) + 8 * total
+        in_bytes = 4 * (2 * B) + 4 * sum(-(-s.total // bs) for s in plan.seqs)
+        row = dict(B=B, new_tokens=total, host_ms=round(wall(host), 4),
+                   device_call_ms=round(wall(device), 4), bytes=out_bytes + in_bytes)
+        res[name] = row
+        log(f"device_metadata {name}: {json.dumps(row)}")
+    return dict(workload="device_metadata", **res)
+
+
 def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
     """Plain device copy (torch copy_) and plain read (torch sum) of a buffer of known
     size: the achievable-bandwidth reference for the roofline, and the known-size
@@ -385,6 +432,7 @@ def main() -> int:
         secondary["packed_prefill"] = run_packed(max(5, args.steps // 2), 2, torch, pkv, log)
         log(json.dumps(secondary["packed_prefill"]))
         secondary["graph_decode"] = run_graph(max(5, args.steps // 2), 3, torch, pkv, log)
+        secondary["device_metadata"] = run_meta(max(5, args.steps // 2), 3, torch, pkv, log)
         for name in ["long_decode", "prefix_prefill", "full_step"]:
             if name == args.workload:
                 continue

@@ -233,6 +233,92 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
                                      hipStream_t stream);
 
 /*
+ * Staged row writes into a device int32 table (docs.vllm.com.cn, "Model
+ * Runner V2 设计文档", section 4, StagedWriteTensor): the table stays on the
+ * device; the host stages ragged writes (row, start, values), packs them
+ * into one contiguous buffer, copies that buffer to the device and launches
+ * one kernel that applies every write.  Used for block tables, whose rows
+ * grow by a few ids per step.
+ *
+ * Packed layout (int32, n writes, `total` values):
+ *   [0, n)              row of each write
+ *   [n, 2n)             first column of each write
+ *   [2n, 3n+1)          offsets: write w's values are values[off[w] .. off[w+1]),
+ *                       off[0] == 0, off[n] == total
+ *   [3n+1, 3n+1+total)  the values, write after write
+ * Size: 3n + 1 + total int32.
+ */
+
+/*
+ * Host: packs n writes (write w puts lens[w] values, taken in order from
+ * `values` after those of the writes before it, into row rows[w] from column
+ * starts[w] on) into `packed` (host memory of packed_capacity int32).
+ * *packed_size receives 3n + 1 + total.
+ * PKV_EINVAL: n < 0; null pointers (n > 0); a write outside [0, num_rows) x
+ * [0, num_cols); a negative length; two writes that cover one element (the
+ * order of overlapping writes would be unspecified); a capacity below the
+ * packed size; int32 overflow of the total.
+ */
+pkv_status pkv_pack_row_writes(int32_t n, const int32_t* rows, const int32_t* starts,
+                               const int32_t* lens, const int32_t* values, int32_t num_rows,
+                               int32_t num_cols, int32_t* packed, int64_t packed_capacity,
+                               int64_t* packed_size);
+
+/*
+ * Device: applies a packed buffer (device memory, the layout above) to
+ * table[num_rows, num_cols] (device, int32, rows row_stride elements apart).
+ * One thread per value; elements outside the table are skipped.  n == 0 or
+ * total == 0 enqueues nothing.
+ * PKV_EINVAL: null pointers (with work to do), n < 0, total < 0,
+ * num_rows < 1, num_cols < 1, row_stride < num_cols.
+ */
+pkv_status pkv_apply_row_writes(int32_t* table, int64_t row_stride, int32_t num_rows,
+                                int32_t num_cols, const int32_t* packed, int32_t n,
+                                int32_t total, hipStream_t stream);
+
+/*
+ * Step metadata built on the device (docs.vllm.com.cn, "Model Runner V2
+ * 设计文档", section 5: inputs prepared by GPU kernels from state kept on the
+ * GPU), with the meaning of pkv_prepare_metadata (AIInfraGuide 3.6,
+ * section 2).  Batch row b is the request in row r = idx_mapping[b] of the
+ * persistent state: c = num_computed[r] tokens already cached, n =
+ * num_scheduled[b] new tokens this step, physical block ids in
+ * block_table[r, 0 ..].
+ * Inputs (device):
+ *   idx_mapping     [B] int32 rows of the persistent state (null: row b)
+ *   num_computed    [num_reqs] int32
+ *   num_scheduled   [B] int32
+ *   block_table     [num_reqs, table_stride] int32
+ * Outputs (device):
+ *   cu_seqlens_q, cu_seqlens_k   [B+1]  prefix sums of n and of c + n
+ *   context_lens    [B]       c + n
+ *   positions       [max_tokens] int64: c + i for new token i (may be null)
+ *   slot_mapping    [max_tokens] int32: block_table[r, p / bs] * bs + p % bs
+ *                   for position p = c + i; -1 if that id is negative
+ *   block_tables    [B, max_blocks_per_seq] int32: the ids covering the c + n
+ *                   tokens, then -1 (may be null)
+ *   max_seqlens     [2] int32: max n, max (c + n) (may be null)
+ * Token rows at or beyond min(sum n, max_tokens) are not written.  One
+ * kernel launch.  Preconditions (device data, not checked): 0 <= r <
+ * num_reqs, c >= 0, n >= 0, ceil((c + n) / bs) <= max_blocks_per_seq <=
+ * table_stride, sums within int32.
+ * PKV_EINVAL: B < 0, null required pointers (B > 0), num_reqs < 1,
+ * block_size not a power of two >= 16, max_blocks_per_seq < 1,
+ * table_stride < max_blocks_per_seq, max_tokens < 0.
+ * PKV_EUNSUPPORTED: B > 4096 (the prefix sums are kept in LDS).
+ * B == 0 writes cu_seqlens_q[0] = cu_seqlens_k[0] = 0 only.
+ */
+pkv_status pkv_prepare_metadata_device(int32_t B, const int32_t* idx_mapping,
+                                       const int32_t* num_computed, const int32_t* num_scheduled,
+                                       const int32_t* block_table, int32_t num_reqs,
+                                       int64_t table_stride, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t max_tokens,
+                                       int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                                       int32_t* context_lens, int64_t* positions,
+                                       int32_t* slot_mapping, int32_t* block_tables,
+                                       int32_t* max_seqlens, hipStream_t stream);
+
+/*
  * Graph-captured decode step with batch buckets (devpress page,
  * "CUDAGraph优化"; AIInfraGuide 3.6, section 5).  A decode step is, for every
  * layer l, pkv_store of the batch's new K/V rows into layer l's caches

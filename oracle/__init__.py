@@ -20,7 +20,7 @@ import numpy as np
 import torch
 
 from . import graph
-from .metadata import prepare_decode, prepare_prefill
+from .metadata import apply_row_writes, prepare_decode, prepare_from_state, prepare_prefill
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "pkv_oracle.c")

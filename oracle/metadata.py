@@ -78,3 +78,42 @@ def prepare_decode(seqs: Sequence, block_size: int, max_blocks_per_seq: int) -> 
         context_lens=context_lens,
         block_tables=_table(seqs, max_blocks_per_seq),
     )
+
+
+# ------------------------------------------------------- state kept on the GPU
+# docs.vllm.com.cn, "Model Runner V2 设计文档": section 4 (StagedWriteTensor:
+# ragged writes staged on the host, applied to a table that stays on the
+# device) and section 5 (step inputs derived on the device from per-request
+# state).  The oracle applies the writes one after the other and derives the
+# step inputs by handing the requests' state to prepare_prefill above.
+
+
+class _Req:
+    """A request as prepare_prefill reads it."""
+
+    def __init__(self, block_ids, num_cached, num_new):
+        self.block_ids = tuple(block_ids)
+        self.num_cached = num_cached
+        self.num_new = num_new
+
+
+def apply_row_writes(table: List[List[int]], writes) -> List[List[int]]:
+    """Each write (row, start, values) overwrites table[row][start:start+len(values)],
+    in the order given.  Returns the table (modified in place)."""
+    for row, start, values in writes:
+        for i, v in enumerate(values):
+            table[row][start + i] = v
+    return table
+
+
+def prepare_from_state(idx_mapping, num_computed, num_scheduled, block_table,
+                       block_size: int, max_blocks_per_seq: int) -> dict:
+    """Step metadata for batch rows b whose request lives in row idx_mapping[b]
+    of the persistent state: num_computed[r] cached tokens, num_scheduled[b]
+    new ones, block ids block_table[r][0..]."""
+    reqs = []
+    for b, r in enumerate(idx_mapping):
+        c, n = num_computed[r], num_scheduled[b]
+        nblk = (c + n + block_size - 1) // block_size
+        reqs.append(_Req(block_table[r][:nblk], c, n))
+    return prepare_prefill(reqs, block_size, max_blocks_per_seq)

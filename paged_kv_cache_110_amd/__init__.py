@@ -14,11 +14,16 @@ Functions:
     prefill_varlen(q, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
                    max_seqlen_q, max_seqlen_k, softmax_scale=None, ...)
     prefill_varlen_packed(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
+    pack_row_writes(writes, num_rows, num_cols) -> host int32 tensor
+    apply_row_writes(table, packed, num_writes, total)
+    StagedWrites(table): stage_write(row, start, values), apply()
+    prepare_metadata_device(idx_mapping, num_computed, num_scheduled, block_table, ...) -> dict
     graph_bucket(max_batch, batch) -> int
     DecodeGraph(k_caches, v_caches, max_batch, H_q, max_blocks_per_seq, ...)
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 from typing import Optional, Sequence
@@ -29,7 +34,8 @@ from ._lib import EXPORTS, LIB_PATH, DecodeStep, PkvError, check, load
 
 __all__ = [
     "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
-    "prefill_varlen_packed", "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
+    "prefill_varlen_packed", "pack_row_writes", "apply_row_writes", "StagedWrites",
+    "prepare_metadata_device", "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
     "version",
 ]
 
@@ -218,6 +224,113 @@ def prefill_varlen_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _ptr(out), _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, total_q, total_k, int(max_seqlen_q),
         int(max_seqlen_k), H_q, H_kv, d, scale, _stream(stream)))
+    return out
+
+
+def _host_i32(values) -> torch.Tensor:
+    return torch.as_tensor(values, dtype=torch.int32).contiguous()
+
+
+def pack_row_writes(writes, num_rows: int, num_cols: int, pin: bool = False) -> torch.Tensor:
+    """Packs ragged writes ``[(row, start, values), ...]`` for a [num_rows, num_cols]
+    table into one host int32 buffer (layout in include/pkv.h); ``pin`` puts it in
+    pinned memory for an asynchronous copy."""
+    n = len(writes)
+    rows = _host_i32([w[0] for w in writes] or [0])
+    starts = _host_i32([w[1] for w in writes] or [0])
+    lens = _host_i32([len(w[2]) for w in writes] or [0])
+    flat = [int(v) for w in writes for v in w[2]]
+    values = _host_i32(flat or [0])
+    size = 3 * n + 1 + len(flat)
+    packed = torch.empty(size, dtype=torch.int32, pin_memory=pin)
+    got = ctypes.c_int64(0)
+    check("pkv_pack_row_writes", load().pkv_pack_row_writes(
+        n, _ptr(rows), _ptr(starts), _ptr(lens), _ptr(values), int(num_rows), int(num_cols),
+        _ptr(packed), size, ctypes.byref(got)))
+    return packed
+
+
+def apply_row_writes(table: torch.Tensor, packed: torch.Tensor, num_writes: int, total: int,
+                     stream=None) -> None:
+    """Applies a packed buffer (device int32) to a device int32 table [rows, cols]."""
+    _need(table.is_cuda and table.dtype == torch.int32 and table.dim() == 2
+          and table.stride(1) == 1, "table must be a GPU int32 [rows, cols] tensor, cols contiguous")
+    _dev_i32(packed, "packed")
+    _need(packed.numel() >= 3 * num_writes + 1 + total, "packed buffer too small")
+    check("pkv_apply_row_writes", load().pkv_apply_row_writes(
+        _ptr(table), table.stride(0), int(table.shape[0]), int(table.shape[1]), _ptr(packed),
+        int(num_writes), int(total), _stream(stream)))
+
+
+class StagedWrites:
+    """Ragged writes into a device int32 table, staged on the host and applied
+    in one kernel (pkv_pack_row_writes + pkv_apply_row_writes).  Each apply packs
+    into fresh pinned memory, so staging the next writes never races the copy of
+    the previous ones."""
+
+    def __init__(self, table: torch.Tensor):
+        _need(table.is_cuda and table.dtype == torch.int32 and table.dim() == 2,
+              "table must be a GPU int32 [rows, cols] tensor")
+        self.table = table
+        self.pending = []
+
+    def stage_write(self, row: int, start: int, values) -> None:
+        self.pending.append((int(row), int(start), [int(v) for v in values]))
+
+    def apply(self, stream: Optional[torch.cuda.Stream] = None) -> None:
+        """Packs, copies and applies every staged write on ``stream`` (default:
+        the current stream)."""
+        if not self.pending:
+            return
+        writes, self.pending = self.pending, []
+        packed = pack_row_writes(writes, self.table.shape[0], self.table.shape[1], pin=True)
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            dev = packed.to(self.table.device, non_blocking=True)
+            total = sum(len(w[2]) for w in writes)
+            apply_row_writes(self.table, dev, len(writes), total)
+
+
+def prepare_metadata_device(idx_mapping: Optional[torch.Tensor], num_computed: torch.Tensor,
+                            num_scheduled: torch.Tensor, block_table: torch.Tensor,
+                            block_size: int, max_blocks_per_seq: int, max_tokens: int,
+                            positions: bool = True, block_tables: bool = True,
+                            out: Optional[dict] = None, stream=None) -> dict:
+    """Step metadata built on the device from request state kept on the device
+    (pkv_prepare_metadata_device).  Returns device tensors ``cu_seqlens_q``,
+    ``cu_seqlens_k``, ``context_lens``, ``slot_mapping`` [max_tokens],
+    ``positions`` [max_tokens] int64, ``block_tables`` [B, max_blocks_per_seq] and
+    ``max_seqlens`` [2]; ``out`` may supply any of them (e.g. a graph's static
+    buffers)."""
+    _dev_i32(num_computed, "num_computed")
+    _dev_i32(num_scheduled, "num_scheduled")
+    _need(block_table.is_cuda and block_table.dtype == torch.int32 and block_table.dim() == 2
+          and block_table.stride(1) == 1, "block_table must be a GPU int32 [reqs, width] tensor")
+    if idx_mapping is not None:
+        _dev_i32(idx_mapping, "idx_mapping")
+    B = int(num_scheduled.shape[0])
+    dev = num_scheduled.device
+    out = dict(out or {})
+
+    def buf(name, shape, dtype):
+        if name not in out:
+            out[name] = torch.empty(shape, dtype=dtype, device=dev)
+        t = out[name]
+        _need(t.is_cuda and t.dtype == dtype and t.is_contiguous() and t.numel() >= math.prod(shape),
+              f"bad {name}")
+        return t
+
+    cq = buf("cu_seqlens_q", (B + 1,), torch.int32)
+    ck = buf("cu_seqlens_k", (B + 1,), torch.int32)
+    ctx = buf("context_lens", (max(B, 1),), torch.int32)
+    slots = buf("slot_mapping", (max(max_tokens, 1),), torch.int32)
+    pos = buf("positions", (max(max_tokens, 1),), torch.int64) if positions else None
+    bt = buf("block_tables", (B, max_blocks_per_seq), torch.int32) if block_tables else None
+    mx = buf("max_seqlens", (2,), torch.int32)
+    check("pkv_prepare_metadata_device", load().pkv_prepare_metadata_device(
+        B, _ptr(idx_mapping), _ptr(num_computed), _ptr(num_scheduled), _ptr(block_table),
+        int(block_table.shape[0]), block_table.stride(0), int(block_size), int(max_blocks_per_seq),
+        int(max_tokens), _ptr(cq), _ptr(ck), _ptr(ctx), _ptr(pos), _ptr(slots), _ptr(bt), _ptr(mx),
+        _stream(stream)))
     return out
 
 

@@ -23,6 +23,9 @@ EXPORTS = (
     "pkv_decode",
     "pkv_prefill_varlen",
     "pkv_prefill_varlen_packed",
+    "pkv_pack_row_writes",
+    "pkv_apply_row_writes",
+    "pkv_prepare_metadata_device",
     "pkv_decode_graph_bucket",
     "pkv_decode_graph_create",
     "pkv_decode_graph_replay",
@@ -88,6 +91,13 @@ def load() -> ctypes.CDLL:
     lib.pkv_prefill_varlen_packed.argtypes = [P, P, I64, P, I64, P, I64, P, P, I32, I32, I32, I32,
                                               I32, I32, I32, I32, F, P]
     lib.pkv_prefill_varlen_packed.restype = ctypes.c_int
+    lib.pkv_pack_row_writes.argtypes = [I32, P, P, P, P, I32, I32, P, I64, P]
+    lib.pkv_pack_row_writes.restype = ctypes.c_int
+    lib.pkv_apply_row_writes.argtypes = [P, I64, I32, I32, P, I32, I32, P]
+    lib.pkv_apply_row_writes.restype = ctypes.c_int
+    lib.pkv_prepare_metadata_device.argtypes = [I32, P, P, P, P, I32, I64, I32, I32, I32, P, P, P,
+                                                P, P, P, P, P]
+    lib.pkv_prepare_metadata_device.restype = ctypes.c_int
     SP = ctypes.POINTER(DecodeStep)
     lib.pkv_decode_graph_bucket.argtypes = [I32, I32]
     lib.pkv_decode_graph_bucket.restype = I32

@@ -4,6 +4,9 @@
 
 #include <limits.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "pkv_internal.h"
 
 namespace {
@@ -214,6 +217,80 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
       static_cast<const uint16_t*>(k), k_stride, static_cast<const uint16_t*>(v), v_stride,
       cu_seqlens_q, cu_seqlens_k, B, total_q, total_k, max_seqlen_q, H_q, H_kv, d, softmax_scale,
       stream));
+}
+
+pkv_status pkv_pack_row_writes(int32_t n, const int32_t* rows, const int32_t* starts,
+                               const int32_t* lens, const int32_t* values, int32_t num_rows,
+                               int32_t num_cols, int32_t* packed, int64_t packed_capacity,
+                               int64_t* packed_size) {
+  if (n < 0 || !packed_size || num_rows < 0 || num_cols < 0) return PKV_EINVAL;
+  if (n > 0 && (!rows || !starts || !lens)) return PKV_EINVAL;
+  int64_t total = 0;
+  for (int32_t w = 0; w < n; ++w) {
+    if (lens[w] < 0 || rows[w] < 0 || rows[w] >= num_rows || starts[w] < 0) return PKV_EINVAL;
+    if ((int64_t)starts[w] + lens[w] > num_cols) return PKV_EINVAL;
+    total += lens[w];
+  }
+  if (total > INT32_MAX || (total > 0 && !values)) return PKV_EINVAL;
+  // no element may be written twice: sort the non-empty writes by (row, start)
+  std::vector<int32_t> order;
+  order.reserve((size_t)n);
+  for (int32_t w = 0; w < n; ++w)
+    if (lens[w] > 0) order.push_back(w);
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return rows[a] != rows[b] ? rows[a] < rows[b] : starts[a] < starts[b];
+  });
+  for (size_t i = 1; i < order.size(); ++i) {
+    const int32_t a = order[i - 1], b = order[i];
+    if (rows[a] == rows[b] && (int64_t)starts[a] + lens[a] > starts[b]) return PKV_EINVAL;
+  }
+  const int64_t size = 3 * (int64_t)n + 1 + total;
+  *packed_size = size;
+  if (!packed || packed_capacity < size) return PKV_EINVAL;
+  int32_t* off = packed + 2 * (int64_t)n;
+  int32_t* vals = off + n + 1;
+  off[0] = 0;
+  for (int32_t w = 0; w < n; ++w) {
+    packed[w] = rows[w];
+    packed[n + w] = starts[w];
+    off[w + 1] = off[w] + lens[w];
+  }
+  for (int64_t i = 0; i < total; ++i) vals[i] = values[i];
+  return PKV_OK;
+}
+
+pkv_status pkv_apply_row_writes(int32_t* table, int64_t row_stride, int32_t num_rows,
+                                int32_t num_cols, const int32_t* packed, int32_t n,
+                                int32_t total, hipStream_t stream) {
+  if (n < 0 || total < 0 || num_rows < 1 || num_cols < 1 || row_stride < num_cols)
+    return PKV_EINVAL;
+  if (n == 0 || total == 0) return PKV_OK;
+  if (!table || !packed) return PKV_EINVAL;
+  return launch_status(
+      pkv::launch_apply_writes(table, row_stride, num_rows, num_cols, packed, n, total, stream));
+}
+
+pkv_status pkv_prepare_metadata_device(int32_t B, const int32_t* idx_mapping,
+                                       const int32_t* num_computed, const int32_t* num_scheduled,
+                                       const int32_t* block_table, int32_t num_reqs,
+                                       int64_t table_stride, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t max_tokens,
+                                       int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                                       int32_t* context_lens, int64_t* positions,
+                                       int32_t* slot_mapping, int32_t* block_tables,
+                                       int32_t* max_seqlens, hipStream_t stream) {
+  if (B < 0 || max_tokens < 0 || !pow2_ge16(block_size) || max_blocks_per_seq < 1 ||
+      table_stride < max_blocks_per_seq || num_reqs < 1)
+    return PKV_EINVAL;
+  if (!cu_seqlens_q || !cu_seqlens_k) return PKV_EINVAL;
+  if (B > 0 && (!num_computed || !num_scheduled || !block_table || !context_lens ||
+                (max_tokens > 0 && !slot_mapping)))
+    return PKV_EINVAL;
+  if (B > pkv::kMetaMaxBatch) return PKV_EUNSUPPORTED;
+  return launch_status(pkv::launch_metadata(
+      B, idx_mapping, num_computed, num_scheduled, block_table, num_reqs, table_stride,
+      block_size, max_blocks_per_seq, max_tokens, cu_seqlens_q, cu_seqlens_k, context_lens,
+      positions, slot_mapping, block_tables, max_seqlens, stream));
 }
 
 }  // extern "C"

@@ -18,6 +18,22 @@ hipError_t launch_store(const uint16_t* key, int64_t key_stride, const uint16_t*
 hipError_t launch_pad_batch(int32_t* slot_mapping, int32_t* context_lens, int32_t from,
                             int32_t to, hipStream_t stream);
 
+// Staged row writes: apply a packed buffer (rows[n], starts[n], off[n+1],
+// values[total]) to a device int32 table.
+hipError_t launch_apply_writes(int32_t* table, int64_t row_stride, int32_t num_rows,
+                               int32_t num_cols, const int32_t* packed, int32_t n, int32_t total,
+                               hipStream_t stream);
+
+// Step metadata from device-resident request state, one launch; B <= kMetaMaxBatch.
+constexpr int32_t kMetaMaxBatch = 4096;
+hipError_t launch_metadata(int32_t B, const int32_t* idx_mapping, const int32_t* num_computed,
+                           const int32_t* num_scheduled, const int32_t* block_table,
+                           int32_t num_reqs, int64_t table_stride, int32_t block_size,
+                           int32_t max_blocks_per_seq, int32_t max_tokens, int32_t* cu_seqlens_q,
+                           int32_t* cu_seqlens_k, int32_t* context_lens, int64_t* positions,
+                           int32_t* slot_mapping, int32_t* block_tables, int32_t* max_seqlens,
+                           hipStream_t stream);
+
 // Decode launch plan: one wavefront per resident slot of the current device.
 struct DecodePlan {
   int32_t num_waves;       // 0 when the shape has no kernel

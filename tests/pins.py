@@ -352,3 +352,96 @@ def pin_graph_padding(g):
 
 
 GRAPH_PINS = [pin_graph_bucket_list, pin_graph_bucket_choice, pin_graph_padding]
+
+
+# ------------------------------------------------- state kept on the device
+
+def _golden(name):
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    with open(path) as f:
+        return json.load(f)
+
+
+def pin_staged_writes_example(m):
+    """The pages' StagedWriteTensor example, on a zero table of its shape."""
+    fx = _golden("staged_writes.json")
+    R, C = fx["shape"]
+    table = [[0] * C for _ in range(R)]
+    m.apply_row_writes(table, [tuple(w) for w in fx["writes"]])
+    nonzero = sorted((r, c, v) for r, row in enumerate(table) for c, v in enumerate(row) if v)
+    assert nonzero == sorted(tuple(e) for e in fx["expected_nonzero"]), nonzero
+
+
+def pin_staged_writes_disjoint_order(m):
+    """Disjoint writes commute; a row not written keeps its contents."""
+    g = torch.Generator().manual_seed(21)
+    R, C = 12, 40
+    writes, used = [], set()
+    for _ in range(30):
+        r = int(torch.randint(0, R, (1,), generator=g))
+        s0 = int(torch.randint(0, C, (1,), generator=g))
+        n = int(torch.randint(0, C - s0 + 1, (1,), generator=g))
+        cells = {(r, s0 + i) for i in range(n)}
+        if cells & used:
+            continue
+        used |= cells
+        writes.append((r, s0, [int(x) for x in torch.randint(-9, 99, (n,), generator=g)]))
+    base = [[1000 + 100 * r + c for c in range(C)] for r in range(R)]
+    a = m.apply_row_writes([row[:] for row in base], writes)
+    b = m.apply_row_writes([row[:] for row in base], list(reversed(writes)))
+    assert a == b, "disjoint writes must commute"
+    for r in range(R):
+        for c in range(C):
+            if (r, c) not in used:
+                assert a[r][c] == base[r][c], (r, c)
+
+
+def _state_of(plan, perm=None):
+    """Persistent state holding plan's sequences; request b in row perm[b]."""
+    B = plan.B
+    perm = list(range(B)) if perm is None else perm
+    R = B + 2  # two rows no batch entry uses
+    computed = [7] * R
+    table = [[-3] * (plan.max_blocks_per_seq + 2) for _ in range(R)]
+    for b, s in enumerate(plan.seqs):
+        r = perm[b]
+        computed[r] = s.num_cached
+        table[r][:len(s.block_ids)] = list(s.block_ids)
+    return perm, computed, [s.num_new for s in plan.seqs], table
+
+
+def pin_state_equals_host_metadata(m):
+    """Metadata from request state equals the pinned host step on the same
+    sequences, wherever the requests live in the persistent state."""
+    plans = [
+        custom_plan([(30, 1), (0, 1), (255, 1), (256, 1)], 16, 4, 2, 64, seed=1, extra_blocks=2),
+        custom_plan([(0, 40), (33, 5), (64, 0), (16, 17)], 16, 4, 2, 64, seed=2),
+        custom_plan([(512, 100), (512, 3), (0, 9)], 256, 4, 2, 64, seed=3, share_first=(2, 2)),
+    ]
+    for i, plan in enumerate(plans):
+        want = m.prepare_prefill(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+        spread = torch.randperm(plan.B + 2, generator=torch.Generator().manual_seed(i))[:plan.B]
+        for perm in (None, list(reversed(range(plan.B))), spread.tolist()):
+            idx, computed, sched, table = _state_of(plan, perm)
+            got = m.prepare_from_state(idx, computed, sched, table, plan.block_size,
+                                       plan.max_blocks_per_seq)
+            assert got == want, f"plan {i} perm {perm}: {got} != {want}"
+
+
+def pin_state_decode_growth(m):
+    """The decode block-growth fixture through the state path: the new token's
+    slot sits in the sequence's last block, at its last position."""
+    fx = _golden("p2_decode_block_growth.json")
+    for c in fx["cases"]:
+        n, bs = c["num_tokens"], c["block_size"]
+        ids = list(range(100, 100 + c["blocks"]))
+        got = m.prepare_from_state([1], [0, n - 1], [1], [[-1], ids + [-1]], bs, c["blocks"])
+        assert got["slot_mapping"][0] // bs == ids[-1], c
+        assert got["slot_mapping"][0] % bs == (n - 1) % bs, c
+        assert got["context_lens"] == [n] and got["positions"] == [n - 1], c
+
+
+META_PINS = [pin_staged_writes_example, pin_staged_writes_disjoint_order,
+             pin_state_equals_host_metadata, pin_state_decode_growth]

@@ -227,3 +227,74 @@ def test_graph_argument_checks_before_any_hip_call():
     assert lib.pkv_decode_step_run(None, 1, None) == 1
     assert lib.pkv_decode_step_run(ctypes.byref(step), 1, None) == 1
     lib.pkv_decode_graph_destroy(None)  # no-op
+
+
+# ------------------------------------------------- staged writes, device metadata
+
+
+def test_pack_row_writes_round_trip():
+    g = torch.Generator().manual_seed(4)
+    R, C = 50, 64
+    writes, used = [], set()
+    while len(writes) < 40:
+        r = int(torch.randint(0, R, (1,), generator=g))
+        s0 = int(torch.randint(0, C, (1,), generator=g))
+        n = int(torch.randint(0, C - s0 + 1, (1,), generator=g))
+        cells = {(r, s0 + i) for i in range(n)}
+        if cells & used:
+            continue
+        used |= cells
+        writes.append((r, s0, [int(x) for x in torch.randint(-100, 10**6, (n,), generator=g)]))
+    packed = pkv.pack_row_writes(writes, R, C).tolist()
+    n, total = len(writes), sum(len(w[2]) for w in writes)
+    assert len(packed) == 3 * n + 1 + total
+    rows, starts, off = packed[:n], packed[n:2 * n], packed[2 * n:3 * n + 1]
+    vals = packed[3 * n + 1:]
+    assert off[0] == 0 and off[-1] == total
+    back = [(rows[w], starts[w], vals[off[w]:off[w + 1]]) for w in range(n)]
+    assert back == writes
+    base = [[-7] * C for _ in range(R)]
+    assert O.apply_row_writes([r[:] for r in base], back) == O.apply_row_writes([r[:] for r in base], writes)
+
+
+def test_pack_row_writes_rejects_bad_writes():
+    def rejects(writes, R=8, C=10):
+        with pytest.raises(pkv.PkvError):
+            pkv.pack_row_writes(writes, R, C)
+
+    rejects([(1, 2, [1, 2, 3]), (1, 4, [9])])       # overlap in one row
+    rejects([(8, 0, [1])])                          # row out of range
+    rejects([(0, 8, [1, 2, 3])])                    # past the last column
+    rejects([(-1, 0, [1])])
+    pkv.pack_row_writes([(1, 2, [1, 2]), (1, 4, [9]), (2, 2, [5]), (3, 0, [])], 8, 10)  # adjacent: ok
+    lib = _lib.load()
+    size = ctypes.c_int64(0)
+    rows = (ctypes.c_int32 * 1)(0)
+    starts = (ctypes.c_int32 * 1)(0)
+    lens = (ctypes.c_int32 * 1)(-1)
+    assert lib.pkv_pack_row_writes(1, rows, starts, lens, None, 4, 4, None, 0, ctypes.byref(size)) == 1
+    lens[0] = 2
+    vals = (ctypes.c_int32 * 2)(5, 6)
+    out = (ctypes.c_int32 * 5)()
+    assert lib.pkv_pack_row_writes(1, rows, starts, lens, vals, 4, 4, out, 5, ctypes.byref(size)) == 1
+    assert size.value == 6  # the size is reported even when the capacity is short
+    out6 = (ctypes.c_int32 * 6)()
+    assert lib.pkv_pack_row_writes(1, rows, starts, lens, vals, 4, 4, out6, 6, ctypes.byref(size)) == 0
+    assert list(out6) == [0, 0, 0, 2, 5, 6]
+
+
+def test_device_metadata_argument_checks_before_any_hip_call():
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(256)
+    a = ctypes.addressof(buf)
+    call = lib.pkv_prepare_metadata_device
+    # B < 0, bad block size, table narrower than max_blocks_per_seq, no outputs
+    assert call(-1, None, a, a, a, 4, 8, 16, 8, 0, a, a, a, None, a, None, None, None) == 1
+    assert call(2, None, a, a, a, 4, 8, 24, 8, 0, a, a, a, None, a, None, None, None) == 1
+    assert call(2, None, a, a, a, 4, 4, 16, 8, 0, a, a, a, None, a, None, None, None) == 1
+    assert call(2, None, a, a, a, 4, 8, 16, 8, 0, None, a, a, None, a, None, None, None) == 1
+    assert call(2, None, None, a, a, 4, 8, 16, 8, 4, a, a, a, None, a, None, None, None) == 1
+    assert call(4097, None, a, a, a, 4, 8, 16, 8, 4, a, a, a, None, a, None, None, None) == 2
+    assert lib.pkv_apply_row_writes(None, 4, 2, 4, None, 0, 0, None) == 0  # nothing to do
+    assert lib.pkv_apply_row_writes(None, 4, 2, 4, None, 1, 3, None) == 1
+    assert lib.pkv_apply_row_writes(a, 3, 2, 4, a, 1, 3, None) == 1  # stride below the width

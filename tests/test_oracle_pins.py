@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from pins import ATTENTION_PINS, GRAPH_PINS
+from pins import ATTENTION_PINS, GRAPH_PINS, META_PINS
 from workloads import SeqState, custom_plan, make_plan, make_tensors, NAN_BF16_BITS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -219,3 +219,11 @@ def test_poisoned_tiny_config_is_finite(orc):
 @pytest.mark.parametrize("pin", GRAPH_PINS, ids=lambda p: p.__name__)
 def test_graph_bucket_oracle(pin):
     pin(O.graph)
+
+
+# ------------------------------------------------- state kept on the device
+
+
+@pytest.mark.parametrize("pin", META_PINS, ids=lambda p: p.__name__)
+def test_device_state_oracle(pin):
+    pin(O)

@@ -81,3 +81,44 @@ def test_graph_plant_is_caught(name):
         except AssertionError as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, f"planted mistake '{name}' passed every pin"
+
+
+# Planted mistakes in the device-state oracle (oracle/metadata.py).
+def _writes_off_by_one(table, writes):
+    for row, start, values in writes:
+        for i, v in enumerate(values):
+            if start + 1 + i < len(table[row]):
+                table[row][start + 1 + i] = v
+    return table
+
+
+def _state_ignoring_idx(idx, computed, sched, table, bs, maxb):
+    return O.prepare_from_state(list(range(len(idx))), computed, sched, table, bs, maxb)
+
+
+def _state_dropping_cached(idx, computed, sched, table, bs, maxb):
+    return O.prepare_from_state(idx, [0] * len(computed), sched, table, bs, maxb)
+
+
+META_PLANTS = {
+    "write_one_column_late": dict(apply_row_writes=_writes_off_by_one),
+    "batch_row_as_state_row": dict(prepare_from_state=_state_ignoring_idx),
+    "cached_tokens_dropped": dict(prepare_from_state=_state_dropping_cached),
+}
+
+
+@pytest.mark.parametrize("name", sorted(META_PLANTS))
+def test_meta_plant_is_caught(name):
+    from pins import META_PINS
+    planted = types.SimpleNamespace(apply_row_writes=O.apply_row_writes,
+                                    prepare_from_state=O.prepare_from_state,
+                                    prepare_prefill=O.prepare_prefill)
+    for k, fn in META_PLANTS[name].items():
+        setattr(planted, k, fn)
+    caught = []
+    for pin in META_PINS:
+        try:
+            pin(planted)
+        except AssertionError as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, f"planted mistake '{name}' passed every pin"
