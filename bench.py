@@ -339,6 +339,35 @@ def run_meta(steps, warmup, torch, pkv, log):
     return dict(workload="device_metadata", **res)
 
 
+def run_sample(steps, warmup, torch, pkv, log):
+    """Gumbel-max sampling of one decode step: 256 rows of bf16 logits over a
+    151936-token vocabulary (pkv_sample_gumbel, both launches), HIP events on
+    the launch stream."""
+    from workloads.sampling import SAMPLE_DECODE as cfg, make_logits
+
+    logits, temps, seeds, offsets = make_logits("cuda")
+    out = torch.empty(cfg["B"], dtype=torch.int64, device="cuda")
+    ws = torch.empty(pkv.sample_workspace_size(cfg["B"], cfg["V"]), dtype=torch.uint8, device="cuda")
+    step_offsets = [offsets + i for i in range(steps)]  # a fresh draw per step
+    for _ in range(warmup):
+        pkv.sample_gumbel(logits, seeds, temps, offsets, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    for i in range(steps):
+        with timer.span("sample"):
+            pkv.sample_gumbel(logits, seeds, temps, step_offsets[i], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("sample")
+    n = cfg["B"] * cfg["V"]
+    nbytes = 2 * n + cfg["B"] * (4 + 8 + 8 + 8)
+    res = dict(workload="gumbel_sample", B=cfg["B"], V=cfg["V"], dtype="bf16", bound="alu",
+               ms=round(ms, 4),
+               logits_per_s=round(n / (ms * 1e-3), 1), gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 2),
+               pct_hbm_peak=round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))
+    log(f"gumbel_sample: {json.dumps(res)}")
+    return res
+
+
 def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
     """Plain device copy (torch copy_) and plain read (torch sum) of a buffer of known
     size: the achievable-bandwidth reference for the roofline, and the known-size
@@ -433,6 +462,7 @@ def main() -> int:
         log(json.dumps(secondary["packed_prefill"]))
         secondary["graph_decode"] = run_graph(max(5, args.steps // 2), 3, torch, pkv, log)
         secondary["device_metadata"] = run_meta(max(5, args.steps // 2), 3, torch, pkv, log)
+        secondary["gumbel_sample"] = run_sample(max(5, args.steps // 2), 3, torch, pkv, log)
         for name in ["long_decode", "prefix_prefill", "full_step"]:
             if name == args.workload:
                 continue

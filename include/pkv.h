@@ -233,6 +233,47 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
                                      hipStream_t stream);
 
 /*
+ * Gumbel-max sampling (devpress page, "Gumbel-Max采样"; docs.vllm.com.cn,
+ * "Model Runner V2 设计文档", section 6, the Gumbel sampling kernel).  For
+ * row b of the logits, with temperature T = temperatures[b]:
+ *   token[b] = argmax_i ( logits[b, i] / T + g_{b,i} ),  g = -ln(-ln u),
+ * which draws token i with probability softmax(logits[b] / T)_i without
+ * forming the softmax.  T <= 0 selects the plain argmax of logits[b] (no
+ * noise).  Ties go to the smallest index.
+ * The uniform u_{b,i} comes from a stateless counter-based generator,
+ * Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+ * Easy as 1, 2, 3", SC 2011): key = (low, high 32 bits of seeds[b]), counter
+ * = (i / 4, low, high 32 bits of offsets[b], 0); word i % 4 of the result, x,
+ * gives u = ((x >> 9) + 0.5) * 2^-23, strictly inside (0, 1).  The same
+ * (seed, offset) always gives the same draw; callers advance the offset per
+ * step.
+ * Arithmetic: fp32 (logits[b, i] / T rounded to fp32, g from accurate fp32
+ * logarithms, their fp32 sum).  Scores that differ by less than the rounding
+ * of these steps (about 1e-5) may be ordered either way.
+ *   logits       device [B, V], fp32 (logits_bf16 == 0) or bf16 (!= 0), rows
+ *                row_stride elements apart, 16-byte aligned rows
+ *   temperatures device [B] fp32, or null for T = 1
+ *   seeds        device [B] int64;  offsets: device [B] int64, or null for 0
+ *   tokens       device [B] int64, written
+ *   workspace    device, pkv_sample_workspace_size(B, V) bytes (no contents
+ *                carried between calls)
+ * Logits must be finite (NaN and infinities are unspecified).
+ * PKV_EINVAL: B < 0, B > 65535, V < 1, row_stride < V or not a multiple of
+ * 8 (bf16) / 4 (fp32), null pointers or misaligned logits (B > 0), a short
+ * workspace.
+ * B == 0 enqueues nothing.
+ */
+/* Workspace bytes pkv_sample_gumbel needs: 8 per row per 4096-logit chunk
+ * (0 for B < 1 or V < 1). */
+size_t pkv_sample_workspace_size(int32_t B, int32_t V);
+
+pkv_status pkv_sample_gumbel(int64_t* tokens, const void* logits, int32_t logits_bf16,
+                             int64_t row_stride, int32_t B, int32_t V,
+                             const float* temperatures, const int64_t* seeds,
+                             const int64_t* offsets, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * Staged row writes into a device int32 table (docs.vllm.com.cn, "Model
  * Runner V2 设计文档", section 4, StagedWriteTensor): the table stays on the
  * device; the host stages ragged writes (row, start, values), packs them

@@ -18,6 +18,7 @@ Functions:
     apply_row_writes(table, packed, num_writes, total)
     StagedWrites(table): stage_write(row, start, values), apply()
     prepare_metadata_device(idx_mapping, num_computed, num_scheduled, block_table, ...) -> dict
+    sample_gumbel(logits, seeds, temperatures=None, offsets=None) -> int64 tokens
     graph_bucket(max_batch, batch) -> int
     DecodeGraph(k_caches, v_caches, max_batch, H_q, max_blocks_per_seq, ...)
 """
@@ -35,7 +36,7 @@ from ._lib import EXPORTS, LIB_PATH, DecodeStep, PkvError, check, load
 __all__ = [
     "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
     "prefill_varlen_packed", "pack_row_writes", "apply_row_writes", "StagedWrites",
-    "prepare_metadata_device", "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
+    "prepare_metadata_device", "sample_gumbel", "sample_workspace_size", "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
     "version",
 ]
 
@@ -331,6 +332,44 @@ def prepare_metadata_device(idx_mapping: Optional[torch.Tensor], num_computed: t
         int(block_table.shape[0]), block_table.stride(0), int(block_size), int(max_blocks_per_seq),
         int(max_tokens), _ptr(cq), _ptr(ck), _ptr(ctx), _ptr(pos), _ptr(slots), _ptr(bt), _ptr(mx),
         _stream(stream)))
+    return out
+
+
+def sample_workspace_size(B: int, V: int) -> int:
+    return int(load().pkv_sample_workspace_size(int(B), int(V)))
+
+
+def sample_gumbel(logits: torch.Tensor, seeds: torch.Tensor,
+                  temperatures: Optional[torch.Tensor] = None,
+                  offsets: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gumbel-max sampling (pkv_sample_gumbel): one token per row of ``logits``
+    [B, V] (bf16 or fp32, unit stride along V), drawn from softmax(logits / T)
+    with Philox noise keyed by ``seeds`` [B] int64 and counted by ``offsets``
+    [B] int64; T <= 0 picks the argmax.  Returns int64 tokens [B]."""
+    _need(logits.is_cuda and logits.dim() == 2 and logits.stride(1) == 1
+          and logits.dtype in (torch.bfloat16, torch.float32),
+          "logits must be a GPU bf16/fp32 [B, V] tensor with unit stride along V")
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    _need(seeds.is_cuda and seeds.dtype == torch.int64 and seeds.shape == (B,)
+          and seeds.is_contiguous(), "seeds must be a contiguous GPU int64 [B] tensor")
+    if offsets is not None:
+        _need(offsets.is_cuda and offsets.dtype == torch.int64 and offsets.shape == (B,)
+              and offsets.is_contiguous(), "offsets must be a contiguous GPU int64 [B] tensor")
+    if temperatures is not None:
+        _need(temperatures.is_cuda and temperatures.dtype == torch.float32
+              and temperatures.shape == (B,) and temperatures.is_contiguous(),
+              "temperatures must be a contiguous GPU fp32 [B] tensor")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int64, device=logits.device)
+    _need(out.dtype == torch.int64 and out.shape == (B,) and out.is_contiguous(), "bad out")
+    need = sample_workspace_size(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=logits.device)
+    have = workspace.numel() * workspace.element_size()
+    check("pkv_sample_gumbel", load().pkv_sample_gumbel(
+        _ptr(out), _ptr(logits), int(logits.dtype == torch.bfloat16), logits.stride(0), B, V,
+        _ptr(temperatures), _ptr(seeds), _ptr(offsets), _ptr(workspace), have, _stream(stream)))
     return out
 
 

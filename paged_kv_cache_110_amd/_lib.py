@@ -23,6 +23,8 @@ EXPORTS = (
     "pkv_decode",
     "pkv_prefill_varlen",
     "pkv_prefill_varlen_packed",
+    "pkv_sample_workspace_size",
+    "pkv_sample_gumbel",
     "pkv_pack_row_writes",
     "pkv_apply_row_writes",
     "pkv_prepare_metadata_device",
@@ -91,6 +93,10 @@ def load() -> ctypes.CDLL:
     lib.pkv_prefill_varlen_packed.argtypes = [P, P, I64, P, I64, P, I64, P, P, I32, I32, I32, I32,
                                               I32, I32, I32, I32, F, P]
     lib.pkv_prefill_varlen_packed.restype = ctypes.c_int
+    lib.pkv_sample_workspace_size.argtypes = [I32, I32]
+    lib.pkv_sample_workspace_size.restype = SZ
+    lib.pkv_sample_gumbel.argtypes = [P, P, I32, I64, I32, I32, P, P, P, P, SZ, P]
+    lib.pkv_sample_gumbel.restype = ctypes.c_int
     lib.pkv_pack_row_writes.argtypes = [I32, P, P, P, P, I32, I32, P, I64, P]
     lib.pkv_pack_row_writes.restype = ctypes.c_int
     lib.pkv_apply_row_writes.argtypes = [P, I64, I32, I32, P, I32, I32, P]

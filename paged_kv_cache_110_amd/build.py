@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["pkv_api.cpp", "pkv_graph.cpp", "pkv_store.hip", "pkv_meta.hip", "pkv_decode.hip", "pkv_prefill.hip"]
+SOURCES = ["pkv_api.cpp", "pkv_graph.cpp", "pkv_store.hip", "pkv_meta.hip", "pkv_sample.hip", "pkv_decode.hip", "pkv_prefill.hip"]
 HEADERS = ["decode_schedule.h", "device_common.h", "pkv_internal.h"]
 
 ARCH = "gfx950"

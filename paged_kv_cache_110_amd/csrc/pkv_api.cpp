@@ -293,4 +293,25 @@ pkv_status pkv_prepare_metadata_device(int32_t B, const int32_t* idx_mapping,
       positions, slot_mapping, block_tables, max_seqlens, stream));
 }
 
+size_t pkv_sample_workspace_size(int32_t B, int32_t V) {
+  if (B < 1 || V < 1) return 0;
+  const int64_t chunk = pkv::sample_chunk_size(false);  // the smaller chunk: the most chunks
+  return (size_t)B * (size_t)((V + chunk - 1) / chunk) * sizeof(uint64_t);
+}
+
+pkv_status pkv_sample_gumbel(int64_t* tokens, const void* logits, int32_t logits_bf16,
+                             int64_t row_stride, int32_t B, int32_t V,
+                             const float* temperatures, const int64_t* seeds,
+                             const int64_t* offsets, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (B < 0 || V < 1 || row_stride < V) return PKV_EINVAL;
+  if (row_stride % (logits_bf16 ? 8 : 4) != 0) return PKV_EINVAL;
+  if (B == 0) return PKV_OK;
+  if (!tokens || !logits || !seeds || !workspace || !aligned16(logits)) return PKV_EINVAL;
+  if (B > 65535) return PKV_EINVAL;  // one grid row per batch row
+  if (workspace_bytes < pkv_sample_workspace_size(B, V)) return PKV_EINVAL;
+  return launch_status(pkv::launch_sample(tokens, logits, logits_bf16 != 0, row_stride, B, V,
+                                          temperatures, seeds, offsets, workspace, stream));
+}
+
 }  // extern "C"

@@ -34,6 +34,13 @@ hipError_t launch_metadata(int32_t B, const int32_t* idx_mapping, const int32_t*
                            int32_t* slot_mapping, int32_t* block_tables, int32_t* max_seqlens,
                            hipStream_t stream);
 
+// Gumbel-max sampling: chunk scores into workspace (B x chunks of 8 bytes),
+// then one wavefront per row picks the token.
+int32_t sample_chunk_size(bool bf16);
+hipError_t launch_sample(int64_t* tokens, const void* logits, bool bf16, int64_t row_stride,
+                         int32_t B, int32_t V, const float* temps, const int64_t* seeds,
+                         const int64_t* offsets, void* workspace, hipStream_t stream);
+
 // Decode launch plan: one wavefront per resident slot of the current device.
 struct DecodePlan {
   int32_t num_waves;       // 0 when the shape has no kernel

@@ -445,3 +445,66 @@ def pin_state_decode_growth(m):
 
 META_PINS = [pin_staged_writes_example, pin_staged_writes_disjoint_order,
              pin_state_equals_host_metadata, pin_state_decode_growth]
+
+
+# ------------------------------------------------------------ Gumbel-max sampling
+
+def pin_philox_known_answers(m):
+    """The generator's published known-answer vectors."""
+    for v in _golden("philox_kat.json")["vectors"]:
+        c = [int(x, 16) for x in v["counter"]]
+        k = [int(x, 16) for x in v["key"]]
+        got = [int(w[0]) for w in m.philox4x32_10([c[0]], [c[1]], [c[2]], [c[3]], k[0], k[1])]
+        assert got == [int(x, 16) for x in v["out"]], (v, [hex(x) for x in got])
+
+
+def pin_gumbel_moments(m):
+    """u stays inside (0, 1); g = -ln(-ln u) has the Gumbel mean (Euler's gamma)
+    and variance pi^2 / 6."""
+    import numpy as np
+    g = []
+    for seed in range(8):
+        w = m.random_words(seed * 7919 + 1, seed, 1 << 17)
+        u = m.uniforms(w)
+        assert float(u.min()) > 0.0 and float(u.max()) < 1.0
+        g.append(m.gumbel(u).astype(np.float64))
+    g = np.concatenate(g)
+    n = g.shape[0]
+    gamma, var = 0.5772156649015329, math.pi ** 2 / 6
+    assert abs(g.mean() - gamma) < 5 * math.sqrt(var / n), g.mean()
+    # variance of the sample variance: (mu4 - var^2) / n, Gumbel excess kurtosis 12/5
+    assert abs(g.var() - var) < 5 * math.sqrt((3 + 2.4 - 1) * var * var / n), g.var()
+
+
+def pin_draws_follow_softmax(m):
+    """The pages' claim: the argmax of logits / T + g is drawn with probability
+    softmax(logits / T).  Chi-square over many offsets of one seed."""
+    import numpy as np
+    logits = np.array([1.0, 2.0, 0.5, -1.0, 3.0, 0.0], dtype=np.float32)
+    N = 12000
+    for T in (1.0, 0.6, 2.5):
+        toks, _ = m.sample(np.tile(logits, (N, 1)), np.full(N, T, np.float32),
+                           np.full(N, 99, np.int64), np.arange(N, dtype=np.int64))
+        counts = np.bincount(toks, minlength=logits.shape[0]).astype(np.float64)
+        z = logits.astype(np.float64) / T
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        chi2 = float(((counts - N * p) ** 2 / (N * p)).sum())
+        assert chi2 < 35.0, (T, chi2, counts.tolist(), (N * p).round(1).tolist())  # 5 dof, p ~ 1e-6
+
+
+def pin_greedy_and_dominant(m):
+    """T <= 0 is the first argmax; a logit far above the rest always wins."""
+    import numpy as np
+    x = np.array([[0.5, 3.0, -1.0, 3.0, 2.0]], np.float32)
+    for T in (0.0, -1.0):
+        toks, _ = m.sample(x, [T], [5], [0])
+        assert toks.tolist() == [1], toks
+    row = np.zeros(100, np.float32)
+    row[37] = 60.0
+    toks, _ = m.sample(np.tile(row, (50, 1)), np.ones(50, np.float32), np.arange(50), np.arange(50))
+    assert toks.tolist() == [37] * 50, toks
+
+
+SAMPLING_PINS = [pin_philox_known_answers, pin_gumbel_moments, pin_draws_follow_softmax,
+                 pin_greedy_and_dominant]

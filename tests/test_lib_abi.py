@@ -298,3 +298,21 @@ def test_device_metadata_argument_checks_before_any_hip_call():
     assert lib.pkv_apply_row_writes(None, 4, 2, 4, None, 0, 0, None) == 0  # nothing to do
     assert lib.pkv_apply_row_writes(None, 4, 2, 4, None, 1, 3, None) == 1
     assert lib.pkv_apply_row_writes(a, 3, 2, 4, a, 1, 3, None) == 1  # stride below the width
+
+
+def test_sample_argument_checks_before_any_hip_call():
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(4096 + 16)
+    a = (ctypes.addressof(buf) + 15) // 16 * 16
+    call = lib.pkv_sample_gumbel
+    assert call(None, None, 1, 104, 0, 100, None, None, None, None, 0, None) == 0  # B == 0
+    assert call(a, a, 1, 8, 2, 0, None, a, None, a, 4096, None) == 1             # V < 1
+    assert call(a, a, 1, 96, 2, 100, None, a, None, a, 4096, None) == 1          # stride < V
+    assert call(a, a, 1, 100, 2, 100, None, a, None, a, 4096, None) == 1         # bf16 stride % 8
+    assert call(a, a, 0, 102, 2, 100, None, a, None, a, 4096, None) == 1         # fp32 stride % 4
+    assert call(a, a + 2, 1, 104, 2, 100, None, a, None, a, 4096, None) == 1     # misaligned
+    assert call(a, a, 1, 104, 2, 100, None, None, None, a, 4096, None) == 1      # no seeds
+    assert call(a, a, 1, 104, 2, 100, None, a, None, a, 8, None) == 1            # short workspace
+    assert lib.pkv_sample_workspace_size(2, 100) == 16
+    assert lib.pkv_sample_workspace_size(3, 151936) == 3 * 38 * 8
+    assert lib.pkv_sample_workspace_size(0, 10) == 0

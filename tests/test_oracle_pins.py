@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle as O
-from pins import ATTENTION_PINS, GRAPH_PINS, META_PINS
+from pins import ATTENTION_PINS, GRAPH_PINS, META_PINS, SAMPLING_PINS
 from workloads import SeqState, custom_plan, make_plan, make_tensors, NAN_BF16_BITS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -227,3 +227,12 @@ def test_graph_bucket_oracle(pin):
 @pytest.mark.parametrize("pin", META_PINS, ids=lambda p: p.__name__)
 def test_device_state_oracle(pin):
     pin(O)
+
+
+# ------------------------------------------------------------ Gumbel-max sampling
+
+
+@pytest.mark.parametrize("pin", SAMPLING_PINS, ids=lambda p: p.__name__)
+def test_sampling_oracle(pin):
+    from oracle import sampling
+    pin(sampling)

@@ -122,3 +122,80 @@ def test_meta_plant_is_caught(name):
         except AssertionError as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, f"planted mistake '{name}' passed every pin"
+
+
+# Planted mistakes in the sampling oracle (oracle/sampling.py): each variant
+# rebuilds the oracle's functions with one plausible error.
+def _sampling_variant(noise=None, temper=None, rounds=10, pick=None):
+    import numpy as np
+    from oracle import sampling as S
+
+    def philox(c0, c1, c2, c3, k0, k1):
+        c = [np.asarray(x, dtype=np.uint64) & 0xFFFFFFFF for x in (c0, c1, c2, c3)]
+        for _ in range(rounds):
+            p0, p1 = c[0] * np.uint64(0xD2511F53), c[2] * np.uint64(0xCD9E8D57)
+            c = [(p1 >> np.uint64(32)) ^ c[1] ^ np.uint64(k0), p1 & np.uint64(0xFFFFFFFF),
+                 (p0 >> np.uint64(32)) ^ c[3] ^ np.uint64(k1), p0 & np.uint64(0xFFFFFFFF)]
+            k0, k1 = (k0 + 0x9E3779B9) & 0xFFFFFFFF, (k1 + 0xBB67AE85) & 0xFFFFFFFF
+        return [x.astype(np.uint32) for x in c]
+
+    def words(seed, offset, V):
+        q = np.arange((V + 3) // 4, dtype=np.uint64)
+        w = philox(q, offset & 0xFFFFFFFF, offset >> 32, 0, seed & 0xFFFFFFFF, seed >> 32)
+        return np.stack(w, axis=1).reshape(-1)[:V]
+
+    gumbel = noise or S.gumbel
+
+    def sample(logits, temps, seeds, offsets=None):
+        logits = np.asarray(logits, np.float32)
+        B = logits.shape[0]
+        offsets = np.zeros(B, np.int64) if offsets is None else np.asarray(offsets)
+        toks, all_s = np.empty(B, np.int64), []
+        for b in range(B):
+            T = np.float32(temps[b])
+            x = logits[b]
+            if T > 0:
+                scaled = temper(x, T) if temper else x / T
+                s = scaled + gumbel(S.uniforms(words(int(seeds[b]), int(offsets[b]), x.shape[0])))
+            else:
+                s = x
+            toks[b] = (pick or np.argmax)(s)
+            all_s.append(s)
+        return toks, all_s
+
+    return types.SimpleNamespace(philox4x32_10=philox, random_words=words, uniforms=S.uniforms,
+                                 gumbel=gumbel, sample=sample)
+
+
+def _plain_exponential_noise(u):
+    import numpy as np
+    return -np.log(u)
+
+
+SAMPLING_PLANTS = {
+    "noise_minus_log_u": dict(noise=_plain_exponential_noise),
+    "temperature_multiplies": dict(temper=lambda x, T: x * T),
+    "philox_seven_rounds": dict(rounds=7),
+    "last_maximum_for_ties": dict(pick=lambda s: len(s) - 1 - int(__import__("numpy").argmax(s[::-1]))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAMPLING_PLANTS))
+def test_sampling_plant_is_caught(name):
+    from pins import SAMPLING_PINS
+    planted = _sampling_variant(**SAMPLING_PLANTS[name])
+    caught = None
+    for pin in SAMPLING_PINS:
+        try:
+            pin(planted)
+        except AssertionError:
+            caught = pin.__name__
+            break
+    assert caught, f"planted mistake '{name}' passed every pin"
+
+
+def test_sampling_variant_without_plant_passes():
+    from pins import SAMPLING_PINS
+    clean = _sampling_variant()
+    for pin in SAMPLING_PINS:
+        pin(clean)
