@@ -494,6 +494,15 @@ def main() -> int:
                         frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
                         flops_per_launch=fl, avg_launch_ms=round(main_res["attn_ms"], 4))
 
+    if plan.kind == "decode":
+        # the same bytes against what plain torch kernels stream on this device
+        probe = copy_probe(torch, log, gib=2.0, iters=5)
+        torch.cuda.empty_cache()
+        roofline["copy_ceiling_gb_per_s"] = probe["copy"]["gb_per_s"]
+        roofline["read_ceiling_gb_per_s"] = probe["read"]["gb_per_s"]
+        roofline["frac_of_copy"] = round(achieved / probe["copy"]["gb_per_s"], 4)
+        roofline["frac_of_read"] = round(achieved / probe["read"]["gb_per_s"], 4)
+
     cpu = None
     if not args.no_cpu_baseline and plan.kind == "decode" and args.workload != "full_step":
         cpu = cpu_baseline(args.workload, args.cpu_budget, log)

@@ -425,7 +425,9 @@ int32_t pkv_decode_graph_bucket(int32_t max_batch, int32_t batch);
 
 /*
  * Captures one graph per bucket on the current HIP device.  Blocking set-up
- * call: it first writes slot -1 and context length 0 to all max_batch rows,
+ * call: it waits for all work already enqueued on the device (so the caller's
+ * fills of the static buffers and the workspace, on any stream, are done),
+ * then writes slot -1 and context length 0 to all max_batch rows,
  * runs the step once eagerly on those all-padding rows (which loads every
  * kernel and writes zero rows to out[*][0, max_batch)), captures the graphs
  * on a stream of its own and waits for that stream.  On success *graph owns

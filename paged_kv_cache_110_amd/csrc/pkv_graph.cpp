@@ -119,6 +119,13 @@ pkv_status pkv_decode_graph_create(const pkv_decode_step* step, pkv_decode_graph
   g->step.out = g->out.data();
   g->buckets = bucket_list(step->max_batch);
 
+  // The set-up below runs on a stream of its own, so first let every write the
+  // caller has enqueued to the static buffers and the workspace (fills, copies
+  // on any stream) finish.
+  if (hipDeviceSynchronize() != hipSuccess) {
+    delete g;
+    return PKV_ELAUNCH;
+  }
   hipStream_t s = nullptr;
   if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
     delete g;

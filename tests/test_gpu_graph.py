@@ -86,3 +86,49 @@ def test_decode_graph_replays(geom):
             graph.replay(mb + 1)
     finally:
         graph.close()
+
+
+def test_full_size_graph_decode():
+    """The graph_decode workload as the benchmark runs it: 28 layers of
+    Qwen3-0.6B attention shapes, a graph set for up to 64 rows; batch 5
+    (padded to bucket 8) and batch 64 replayed, each bit-identical to the eager
+    step, and sampled rows of the first and the last layer against the oracle."""
+    from workloads.graph import GRAPH_DECODE as cfg, graph_plan
+
+    plan = graph_plan()
+    L, mb = cfg["layers"], cfg["max_batch"]
+    bs, maxb = plan.block_size, plan.max_blocks_per_seq
+    tens = make_tensors(plan, DEV, poison=True)
+    log(f"full-size graph decode: {L} layers, {plan.num_blocks} blocks")
+    meta = pkv.prepare_metadata(plan.seqs, bs, maxb)
+    graph = pkv.DecodeGraph([tens.k_cache(l) for l in range(L)], [tens.v_cache(l) for l in range(L)],
+                            mb, plan.H_q, maxb)
+    outs = {}
+    try:
+        for batch in (5, 64):
+            graph.slot_mapping[:batch].copy_(meta["slot_mapping"][:batch])
+            graph.context_lens[:batch].copy_(meta["context_lens"][:batch])
+            graph.block_tables[:batch].copy_(meta["block_tables"][:batch])
+            graph.q[:, :batch].copy_(tens.q[:, :batch])
+            graph.kv_new[:, :batch].copy_(tens.kv_new[:, :batch])
+            graph.replay(batch)
+            torch.cuda.synchronize()
+            replayed = graph.out[:, :batch].clone()
+            graph.run_eager(batch)
+            torch.cuda.synchronize()
+            assert torch.equal(graph.out[:, :batch].view(torch.int16), replayed.view(torch.int16)), batch
+            outs[batch] = replayed
+    finally:
+        graph.close()
+    host = cpu_copy(tens, layers=[0, L - 1])  # host layer i = device layer [0, L-1][i]
+    om = O.prepare_decode(plan.seqs, bs, maxb)
+    rows = [0, 3, 4, 17, 40, 63]
+    for hl, layer in enumerate((0, L - 1)):
+        O.default().store(host.k_cache(hl), host.v_cache(hl), host.k_new(layer), host.v_new(layer),
+                          om["slot_mapping"])
+        ref = O.default().decode(host.q[layer][rows], host.k_cache(hl), host.v_cache(hl),
+                                 [om["block_tables"][r] for r in rows], [om["context_lens"][r] for r in rows],
+                                 scale_of(plan.d))
+        assert_close(outs[64][layer][rows], ref, f"graph batch 64 layer {layer}")
+        small = [r for r in rows if r < 5]
+        assert_close(outs[5][layer][small], ref[:len(small)], f"graph batch 5 layer {layer}")
