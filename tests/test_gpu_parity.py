@@ -56,6 +56,7 @@ def test_tiny_decode_config():
 DECODE_GEOMS = [  # (block_size, H_q, H_kv, d)
     (16, 4, 2, 64), (16, 8, 1, 64), (32, 16, 4, 64), (16, 8, 8, 64),
     (256, 16, 8, 128), (16, 4, 4, 128), (64, 32, 8, 128), (256, 64, 8, 128),
+    (1024, 16, 2, 128),
 ]
 
 
@@ -82,7 +83,7 @@ def test_decode_random_shapes(geom):
 
 PREFILL_GEOMS = [  # (block_size, H_q, H_kv, d)
     (16, 4, 2, 64), (16, 8, 8, 64), (256, 16, 8, 128), (32, 16, 2, 128),
-    (16, 8, 1, 128), (256, 32, 4, 64),
+    (16, 8, 1, 128), (256, 32, 4, 64), (1024, 8, 2, 128),
 ]
 
 
@@ -91,8 +92,17 @@ def test_prefill_random_shapes(geom):
     bs, H_q, H_kv, d = geom
     log(f"prefill geom {geom}")
     specs = [(0, 1), (0, 37), (5, 64), (bs, 130), (3 * bs + 7, 300), (2 * bs, 2 * bs),
-             (700, 1), (0, 513)]
+             (64, 0), (700, 1), (0, 513)]
     plan = custom_plan(specs, bs, H_q, H_kv, d, seed=7 + bs, extra_blocks=3, kind="prefill")
+    _full_check(plan)
+
+
+def test_prefill_long_sequence():
+    # more new tokens than the benchmark's sequences (several query tiles past 2048),
+    # behind a cached prefix that ends mid-block
+    log("prefill of 3000 new tokens after 333 cached")
+    plan = custom_plan([(333, 3000), (0, 5)], 64, 4, 2, 64, seed=13, extra_blocks=2,
+                       kind="prefill")
     _full_check(plan)
 
 
