@@ -40,6 +40,8 @@
 //    decode_merge_kernel combines the pieces in share order.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "decode_schedule.h"
 #include "device_common.h"
 #include "pkv_internal.h"
@@ -607,34 +609,70 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     return (k * 2 + (p == 0 ? 1 : 0)) * G + g;
   };
 
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, ws_ml[2 * prow(p)]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor_f32(M, off));
-
-  float L = 0.f;
+  // One pass: each piece group keeps a running (max, sum, acc) over its
+  // pieces, so all of a row's loads can be in flight together; the 8 groups
+  // are then rescaled to the common max and summed.  (A piece's max is
+  // finite: every piece holds at least one tile of keys.)
+  float mg = -INFINITY, lg = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-#pragma unroll 2
-  for (int p = pg; p < nparts; p += 8) {
-    const int64_t r = prow(p);
-    const float2 st = *reinterpret_cast<const float2*>(ws_ml + 2 * r);
-    const float w = fast_exp2(st.x - M);
-    L += st.y * w;
-    const float* src = ws_acc + r * D + sub * EPL;
+  if (nparts <= 8) {  // at most one piece per group: one round of loads
+    if (pg < nparts) {
+      const int64_t r = prow(pg);
+      const float2 st = *reinterpret_cast<const float2*>(ws_ml + 2 * r);
+      const float* src = ws_acc + r * D + sub * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; e += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
-      o[e + 0] += v[0] * w;
-      o[e + 1] += v[1] * w;
-      o[e + 2] += v[2] * w;
-      o[e + 3] += v[3] * w;
+      for (int e = 0; e < EPL; e += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + e);
+        o[e] = v[0];
+        o[e + 1] = v[1];
+        o[e + 2] = v[2];
+        o[e + 3] = v[3];
+      }
+      mg = st.x;
+      lg = st.y;
     }
   }
-  L = cross_reduce<8, false>(L);
+  // More pieces: each group fetches KB of them before combining any, so a
+  // row's loads overlap.
+  auto batched = [&](auto kb_tag) {
+    constexpr int KB = decltype(kb_tag)::value;
+    for (int p0 = pg; p0 < nparts; p0 += 8 * KB) {
+      float2 st[KB];
+      f32x4 v[KB][EPL / 4];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = cross_reduce<8, false>(o[e]);
+      for (int j = 0; j < KB; ++j) {  // unconditional loads (a piece past the end reads piece pg)
+        const int p = p0 + 8 * j;
+        const int64_t r = prow(p < nparts ? p : pg);
+        st[j] = *reinterpret_cast<const float2*>(ws_ml + 2 * r);
+        const float* src = ws_acc + r * D + sub * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e) v[j][e] = *reinterpret_cast<const f32x4*>(src + 4 * e);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any use
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        // a piece past the end weighs 0 (max -inf); piece j = 0 always exists,
+        // so mg is finite before any such piece and its a is 1
+        const bool in = p0 + 8 * j < nparts;
+        const float mj = in ? st[j].x : -INFINITY;
+        const float mn = fmaxf(mg, mj);
+        const float a = fast_exp2(mg - mn);  // 0 for the group's first piece
+        const float w = fast_exp2(mj - mn);
+        lg = lg * a + (in ? st[j].y : 0.f) * w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] = o[e] * a + v[j][e / 4][e % 4] * w;
+        mg = mn;
+      }
+    }
+  };
+  if (nparts > 8) batched(std::integral_constant<int, 2>{});
+  const float M = cross_reduce<8, true>(mg);
+  const float sg = fast_exp2(mg - M);  // 0 for a group without pieces
+  const float L = cross_reduce<8, false>(lg * sg);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = cross_reduce<8, false>(o[e] * sg);
   if (pg != 0) return;
   const float inv = 1.0f / L;
 #pragma unroll
