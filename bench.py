@@ -10,10 +10,16 @@ for every layer.  Inputs are resident in HBM before timing starts.
 The JSON line reports the Qwen3-0.6B-shaped decode workload (B=256, H_q=16,
 H_kv=8, d=128, block size 256, context lengths U[128, 2048]) with its decode
 roofline (achieved algorithmic HBM bytes per decode call / the call's average
-duration, from HIP events on the launch stream) and the CPU oracle timed on a
-bounded sample.  The other workloads are reported under "secondary".
+duration) and the CPU oracle timed on a bounded sample.  The other workloads
+are reported under "secondary".
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+Timing: the timed region (K steps) holds no events, only the library calls,
+bracketed by synchronisations and the wall clock.  Per-call durations come
+from the same calls run back to back right after it, with one pair of HIP
+events on the launch stream around each run (events recorded between calls
+add their own gaps to what they measure).
+
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -77,34 +83,17 @@ def measured_traffic(workload: str):
 
 # ------------------------------------------------------------------- timing
 
-class Timer:
-    """HIP events recorded on the current stream (the stream the library launches on)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def span(self, name):
-        torch = self.torch
-        timer = self
-
-        class _Span:
-            def __enter__(self):
-                self.a = torch.cuda.Event(enable_timing=True)
-                self.b = torch.cuda.Event(enable_timing=True)
-                self.a.record()
-
-            def __exit__(self, *exc):
-                self.b.record()
-                timer.pairs.setdefault(name, []).append((self.a, self.b))
-
-        return _Span()
-
-    def mean_ms(self, name):
-        ev = self.pairs.get(name, [])
-        if not ev:
-            return float("nan")
-        return sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+def events_ms(torch, fn, n):
+    """Average duration of n back-to-back calls fn(i), from one pair of HIP events on
+    the current stream (the stream the library launches on)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
 
 
 def run_workload(name, steps, warmup, pools, torch, pkv, log):
@@ -127,45 +116,46 @@ def run_workload(name, steps, warmup, pools, torch, pkv, log):
     log(f"{name}: inputs ready in {time.time() - t0:.1f}s ({plan.B} seqs, {plan.num_blocks} blocks,"
         f" {pools} pool(s))")
 
-    timer = Timer(torch)
-
-    def step(i, timed):
+    def store(i, layer):
         t = tens[i % pools]
-        for layer in range(plan.layers):
-            kc, vc = t.k_cache(layer), t.v_cache(layer)
-            if timed:
-                with timer.span("store"):
-                    pkv.store(t.k_new(layer), t.v_new(layer), kc, vc, dm["slot_mapping"])
-            else:
-                pkv.store(t.k_new(layer), t.v_new(layer), kc, vc, dm["slot_mapping"])
-            if plan.kind == "decode":
-                args = (t.q[layer], kc, vc, dm["block_tables"], dm["context_lens"], scale)
-                kw = dict(out=outs[i % pools], workspace=ws)
-                if timed:
-                    with timer.span("attn"):
-                        pkv.decode(*args, **kw)
-                else:
-                    pkv.decode(*args, **kw)
-            else:
-                args = (t.q[layer], kc, vc, dm["block_tables"], dm["cu_seqlens_q"],
-                        dm["cu_seqlens_k"], dm["max_seqlen_q"], dm["max_seqlen_k"], scale)
-                if timed:
-                    with timer.span("attn"):
-                        pkv.prefill_varlen(*args)
-                else:
-                    pkv.prefill_varlen(*args)
+        pkv.store(t.k_new(layer), t.v_new(layer), t.k_cache(layer), t.v_cache(layer),
+                  dm["slot_mapping"])
 
+    def attention(i, layer):
+        t = tens[i % pools]
+        kc, vc = t.k_cache(layer), t.v_cache(layer)
+        if plan.kind == "decode":
+            pkv.decode(t.q[layer], kc, vc, dm["block_tables"], dm["context_lens"], scale,
+                       out=outs[i % pools], workspace=ws)
+        else:
+            pkv.prefill_varlen(t.q[layer], kc, vc, dm["block_tables"], dm["cu_seqlens_q"],
+                               dm["cu_seqlens_k"], dm["max_seqlen_q"], dm["max_seqlen_k"], scale)
+
+    def step(i):
+        for layer in range(plan.layers):
+            store(i, layer)
+            attention(i, layer)
+
+    # the timed region: whole steps, wall clock between synchronisations, no
+    # events inside (recording timing events between calls perturbs them)
     for i in range(warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     start = time.perf_counter()
     for i in range(steps):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - start
     ms_step = wall * 1e3 / steps
-    res = dict(plan=plan, ms_per_step=ms_step, attn_ms=timer.mean_ms("attn"),
-               store_ms=timer.mean_ms("store"))
+
+    # per-call durations: the same calls back to back (pools rotating as in the
+    # steps), one pair of HIP events on the launch stream around each run
+    L = plan.layers
+    attn_ms = events_ms(torch, lambda k: attention(k // L, k % L), steps * L)
+    # store calls back to back are bound by the host's call overhead, not the
+    # GPU: the store's share is the step time per layer minus the attention call
+    store_ms = max(ms_step / L - attn_ms, 0.0)
+    res = dict(plan=plan, ms_per_step=ms_step, attn_ms=attn_ms, store_ms=store_ms)
     del tens, ws
     torch.cuda.empty_cache()
     return res
@@ -216,12 +206,8 @@ def run_packed(steps, warmup, torch, pkv, log):
     for _ in range(warmup):
         pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out)
     torch.cuda.synchronize()
-    timer = Timer(torch)
-    for _ in range(steps):
-        with timer.span("attn"):
-            pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out)
-    torch.cuda.synchronize()
-    ms = timer.mean_ms("attn")
+    ms = events_ms(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out),
+                   steps)
     fl = 4 * cfg["d"] * cfg["H_q"] * sum(n * (n + 1) // 2 for n in lens)
     tf = fl / (ms * 1e-3) / 1e12
     return dict(workload="packed_prefill", B=cfg["B"], tokens=sum(lens), attn_ms=round(ms, 4),
@@ -352,12 +338,8 @@ def run_sample(steps, warmup, torch, pkv, log):
     for _ in range(warmup):
         pkv.sample_gumbel(logits, seeds, temps, offsets, out=out, workspace=ws)
     torch.cuda.synchronize()
-    timer = Timer(torch)
-    for i in range(steps):
-        with timer.span("sample"):
-            pkv.sample_gumbel(logits, seeds, temps, step_offsets[i], out=out, workspace=ws)
-    torch.cuda.synchronize()
-    ms = timer.mean_ms("sample")
+    ms = events_ms(torch, lambda i: pkv.sample_gumbel(logits, seeds, temps, step_offsets[i], out=out,
+                                                      workspace=ws), steps)
     n = cfg["B"] * cfg["V"]
     nbytes = 2 * n + cfg["B"] * (4 + 8 + 8 + 8)
     res = dict(workload="gumbel_sample", B=cfg["B"], V=cfg["V"], dtype="bf16", bound="alu",
@@ -397,8 +379,8 @@ def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_decode",
                     choices=["qwen3_decode", "long_decode", "prefix_prefill", "full_step"])
     ap.add_argument("--pools", type=int, default=2,
