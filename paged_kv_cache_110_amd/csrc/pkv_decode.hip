@@ -15,7 +15,8 @@
 //    Each first streams a static share of the list, then takes shrinking
 //    shares from an atomic counter (decode_schedule.h): the two wavefronts of
 //    a SIMD progress at very different rates, so equal static shares would
-//    leave the call waiting for the slowest;
+//    leave the call waiting for the slowest.  A small call (a few tiles per
+//    wavefront) is one static pass spread over as many wavefronts as it fills;
 //  - 16 divides every supported block size and tiles start at multiples of 16,
 //    so a tile never crosses a page (the devpress page's point about read
 //    lengths dividing the block size): its physical block id is one scalar load

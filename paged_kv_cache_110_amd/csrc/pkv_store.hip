@@ -6,6 +6,9 @@
 // or V row with a single 128-bit load and store.  Consecutive threads cover
 // consecutive chunks of a row, so every wavefront reads and writes whole
 // contiguous 1 KiB spans of a row (a 2 KiB row for H_kv*d = 1024 is two waves).
+//
+// Also here: the padding kernel of a bucketed (graph-captured) decode step,
+// which marks the rows between the batch and its bucket as padding.
 #include "device_common.h"
 #include "pkv_internal.h"
 
