@@ -376,6 +376,10 @@ def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
     return res
 
 
+SECONDARY = ("packed_prefill", "graph_decode", "device_metadata", "gumbel_sample",
+             "long_decode", "prefix_prefill", "full_step")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +390,9 @@ def main() -> int:
     ap.add_argument("--pools", type=int, default=2,
                     help="independent copies of the cache rotated across steps (single-layer workloads)")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="all",
+                    help="comma-separated secondary workloads to run (default: all of "
+                         + ", ".join(SECONDARY) + ")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -439,14 +446,25 @@ def main() -> int:
     log(json.dumps(s))
 
     secondary = {}
-    if not args.no_secondary:
-        secondary["packed_prefill"] = run_packed(max(5, args.steps // 2), 2, torch, pkv, log)
-        log(json.dumps(secondary["packed_prefill"]))
-        secondary["graph_decode"] = run_graph(max(5, args.steps // 2), 3, torch, pkv, log)
-        secondary["device_metadata"] = run_meta(max(5, args.steps // 2), 3, torch, pkv, log)
-        secondary["gumbel_sample"] = run_sample(max(5, args.steps // 2), 3, torch, pkv, log)
+    wanted = set() if args.no_secondary else (
+        set(SECONDARY) if args.secondary == "all" else set(args.secondary.split(",")))
+    unknown = wanted - set(SECONDARY)
+    if unknown:
+        print(f"unknown secondary workloads: {sorted(unknown)}", file=sys.stderr)
+        return 2
+    if wanted:
+        n2 = max(5, args.steps // 2)
+        if "packed_prefill" in wanted:
+            secondary["packed_prefill"] = run_packed(n2, 2, torch, pkv, log)
+            log(json.dumps(secondary["packed_prefill"]))
+        if "graph_decode" in wanted:
+            secondary["graph_decode"] = run_graph(n2, 3, torch, pkv, log)
+        if "device_metadata" in wanted:
+            secondary["device_metadata"] = run_meta(n2, 3, torch, pkv, log)
+        if "gumbel_sample" in wanted:
+            secondary["gumbel_sample"] = run_sample(n2, 3, torch, pkv, log)
         for name in ["long_decode", "prefix_prefill", "full_step"]:
-            if name == args.workload:
+            if name == args.workload or name not in wanted:
                 continue
             r = run_workload(name, max(5, args.steps // 2), 2,
                              1 if name in ("full_step", "prefix_prefill") else args.pools,

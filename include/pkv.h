@@ -247,9 +247,11 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
  * gives u = ((x >> 9) + 0.5) * 2^-23, strictly inside (0, 1).  The same
  * (seed, offset) always gives the same draw; callers advance the offset per
  * step.
- * Arithmetic: fp32 (logits[b, i] / T rounded to fp32, g from accurate fp32
- * logarithms, their fp32 sum).  Scores that differ by less than the rounding
- * of these steps (about 1e-5) may be ordered either way.
+ * Arithmetic: fp32.  logits[b, i] / T is the correctly rounded quotient
+ * (for tiny quotients, below 2^-80, its last bits may differ); g is
+ * -ln(ln 2) - ln 2 * log2(-log2 u) on the hardware base-2 logarithm, within a
+ * few ulp of an fp32 -ln(-ln u); the score is their fp32 sum.  Scores that
+ * differ by less than this rounding (about 1e-5) may be ordered either way.
  *   logits       device [B, V], fp32 (logits_bf16 == 0) or bf16 (!= 0), rows
  *                row_stride elements apart, 16-byte aligned rows
  *   temperatures device [B] fp32, or null for T = 1

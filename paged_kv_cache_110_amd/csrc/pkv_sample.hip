@@ -10,11 +10,13 @@
 // fp32 values), the workgroup finds the chunk's largest logit, and only groups
 // of 4 logits that can still win (see kPruneSpan) get their Philox block and
 // noise; each wavefront packs its surviving groups into a list in LDS and
-// shares them out over its lanes, unless most groups survive.  The best
-// (score, index) is kept as one ordered 64-bit key; the workgroup's best key
-// goes to the workspace.
+// shares them out over its lanes, unless most groups survive.  Each thread
+// keeps its best (score, index); the workgroup reduces them as ordered 64-bit
+// keys and its best key goes to the workspace.
 // sample_reduce_kernel: one wavefront per row takes the best chunk key and
 // writes the token.  Keys order by score, then by smaller index.
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -35,7 +37,12 @@ int32_t sample_chunk_size(bool bf16) {
 
 // Philox4x32-10: ten rounds of two 32x32->64 products, the high halves xored
 // into the other counter words with the round key, the key bumped by the
-// Weyl constants after every round.
+// Weyl constants after every round.  Each three-way xor is one v_bitop3_b32
+// (truth table 0x96); the key schedule stays in scalar registers.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
   constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
   constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
@@ -43,8 +50,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)kM0 * c[0];
     const uint64_t p1 = (uint64_t)kM1 * c[2];
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c[1], k0);
+    const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c[3], k1);
     c[0] = n0;
     c[1] = (uint32_t)p1;
     c[2] = n2;
@@ -54,12 +61,35 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
   }
 }
 
-// g = -ln(-ln u), u = ((x >> 9) + 0.5) * 2^-23 (exact in fp32, inside (0, 1)).
-// logf, not the hardware log2: near u = 1 the inner logarithm is tiny and
-// must keep its relative accuracy, since those draws give the largest g.
+// g = -ln(-ln u), u = ((x >> 9) + 0.5) * 2^-23 (exact in fp32, inside (0, 1)),
+// taken as -ln(ln 2) - ln 2 * log2(-log2 u): two hardware base-2 logarithms
+// (v_log_f32, relative error about 1 ulp, accurate near 1 as well) and one
+// fma.  Neither logarithm sees a denormal or a value outside (0, 24], so the
+// library logf's range handling is not needed.  The result differs from an
+// fp32 -ln(-ln u) by a few units in the last place at most.
 __device__ __forceinline__ float gumbel_of(uint32_t x) {
-  const float u = ((float)(x >> 9) + 0.5f) * 0x1p-23f;
-  return -logf(-logf(u));
+  constexpr float kLn2 = 0.693147180559945309f;
+  constexpr float kNegLnLn2 = 0.366512920581664327f;  // -ln(ln 2)
+  const float u = fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);
+  const float w = -__builtin_amdgcn_logf(u);  // -log2 u, in [8.6e-8, 24]
+  return fmaf(-kLn2, __builtin_amdgcn_logf(w), kNegLnLn2);
+}
+
+// x / T.  FAST: the product with r = 1/T (correctly rounded) plus one fma
+// correction of its residual.  For temperatures in [2^-32, 2^32] and |x| and
+// |x| / T in [2^-80, 2^126) it gave the IEEE quotient on every pair checked
+// (each finite bf16 value and random fp32 values, at over 600 temperatures);
+// below 2^-80 its last bits may differ, far below the noise added to it.  The
+// kernel takes it only for chunks whose largest logit keeps every quotient
+// that can win below 2^126.
+template <bool FAST>
+__device__ __forceinline__ float div_t(float x, float T, float r) {
+  if constexpr (FAST) {
+    const float q = x * r;
+    return fmaf(fmaf(-q, T, x), r, q);
+  } else {
+    return x / T;
+  }
 }
 
 // Ordered key: larger score first, then smaller index.
@@ -147,21 +177,42 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(
   __shared__ uint64_t red[kSampleThreads / 64];
   __shared__ float redf[kSampleThreads / 64];
   __shared__ int32_t work[kSampleThreads / 64][64 * NG];  // compacted groups, per wavefront
-  uint64_t best = 0;
-  // scores one group of 4 consecutive logits (first index i, values v[4])
-  auto score_group = [&](int64_t i, const float (&v)[4]) {
-    uint32_t r[4] = {(uint32_t)(i >> 2), c1, c2, 0u};
+  // the thread's best candidate; equal scores go to the smaller index
+  float bs = -INFINITY;
+  uint32_t bi = 0xFFFFFFFFu;
+  // (bitwise, so that the update compiles to selects, not branches)
+  auto consider = [&](bool valid, float s, uint32_t i) {
+    const bool take = valid & ((s > bs) | ((s == bs) & (i < bi)));
+    bs = take ? s : bs;
+    bi = take ? i : bi;
+  };
+  // scores one group of 4 consecutive logits (first index i, values v[4]).
+  // IN_ORDER: the thread meets its indices in increasing order and logits past
+  // the row's end hold -inf, so a strict "greater" keeps the first of equal
+  // scores and never takes an index past the end (-inf / T + g is -inf, or
+  // NaN on the multiply path, and neither beats the initial -inf).
+  auto score_group = [&](auto fast, auto in_order, uint32_t i, const float (&v)[4], float T,
+                         float rT) {
+    uint32_t r[4] = {i >> 2, c1, c2, 0u};
     philox4x32_10(r, k0, k1);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (i + e < V) best = umax64(best, score_key(v[e] / T + gumbel_of(r[e]), (uint32_t)(i + e)));
+    for (int e = 0; e < 4; ++e) {
+      const float s = div_t<decltype(fast)::value>(v[e], T, rT) + gumbel_of(r[e]);
+      if constexpr (decltype(in_order)::value) {
+        const bool take = s > bs;
+        bs = take ? s : bs;
+        bi = take ? i + e : bi;
+      } else {
+        consider(i + e < (uint32_t)V, s, i + e);
+      }
+    }
   };
 
   if (greedy) {
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
       const int64_t i = index_of(j);
-      if (i < V) best = umax64(best, score_key(x[j], (uint32_t)i));
+      consider(i < V, x[j], (uint32_t)i);
     }
   } else {
     // 2. the chunk's largest logit, and the pruning threshold in logit units
@@ -192,17 +243,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(
       if (lane >= o) incl += y;
     }
     const int total = __shfl(incl, 63, 64);
-    if (total * 2 > 64 * NG) {
-      // most groups survive: score them where they are
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (gmask & (1u << g)) {
-          const float v[4] = {x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-          score_group(index_of(4 * g), v);
-        }
-      }
-    } else {
-      // 4. compact the surviving groups of the wavefront, then share them out
+    if (total * 2 <= 64 * NG) {
+      // few groups survive: compact them (first index of each) for sharing out
       int slot = incl - cnt;
 #pragma unroll
       for (int g = 0; g < NG; ++g)
@@ -210,15 +252,39 @@ __global__ __launch_bounds__(kSampleThreads) void sample_chunk_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int e = lane; e < total; e += 64) {
-        const int64_t i = work[wave][e];
-        float v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = i + k < V ? load_logit(i + k) : -INFINITY;
-        score_group(i, v);
-      }
     }
+    // 4. score the surviving groups, in place or from the compacted list.  The
+    // multiply-and-correct division needs T in [2^-32, 2^32] and a chunk whose
+    // largest logit is at most 2^64 in size: every quotient that can win then
+    // stays finite (a logit below -2^96 may give NaN, which never wins, where
+    // the quotient would be hugely negative and lose as well).
+    auto run = [&](auto fast) {
+      const float rT = 1.0f / T;
+      if (total * 2 > 64 * NG) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (gmask & (1u << g)) {
+            const float v[4] = {x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+            score_group(fast, std::true_type{}, (uint32_t)index_of(4 * g), v, T, rT);
+          }
+        }
+      } else {
+        for (int e = lane; e < total; e += 64) {
+          const int64_t i = work[wave][e];
+          float v[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = i + k < V ? load_logit(i + k) : -INFINITY;
+          score_group(fast, std::false_type{}, (uint32_t)i, v, T, rT);
+        }
+      }
+    };
+    const bool fast_div = T >= 0x1p-32f && T <= 0x1p32f && fabsf(m) <= 0x1p64f;
+    if (fast_div)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   }
+  uint64_t best = bi == 0xFFFFFFFFu ? 0ull : score_key(bs, bi);
   best = wave_max_key(best);
   if (lane == 0) red[wave] = best;
   __syncthreads();
@@ -236,7 +302,8 @@ __global__ __launch_bounds__(64) void sample_reduce_kernel(const uint64_t* __res
   uint64_t best = 0;
   for (int c = threadIdx.x; c < nchunks; c += 64) best = umax64(best, partial[(int64_t)b * nchunks + c]);
   best = wave_max_key(best);
-  if (threadIdx.x == 0) tokens[b] = (int64_t)(0xFFFFFFFFu - (uint32_t)best);
+  // key 0: no candidate at all (possible only with NaN logits); token 0
+  if (threadIdx.x == 0) tokens[b] = best ? (int64_t)(0xFFFFFFFFu - (uint32_t)best) : 0;
 }
 
 hipError_t launch_sample(int64_t* tokens, const void* logits, bool bf16, int64_t row_stride,

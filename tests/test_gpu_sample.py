@@ -112,3 +112,58 @@ def test_full_size_sample_rows():
     _check(tok[rows], sub, temps[rows].cpu().numpy(), seeds[rows].cpu().numpy(),
            offsets[rows].cpu().numpy(), "sample full size")
     assert cfg["B"] == logits.shape[0]
+
+
+# Logits per chunk of the first launch (one workgroup: 256 threads x 4 loads of
+# 16 bytes), which fixes where each chunk's best key sits in the workspace.
+_CHUNK = {True: 8192, False: 4096}
+
+
+def _decode_keys(keys):
+    """Chunk keys -> (score, index): the high word is the score's bits made
+    order-preserving (sign bit flipped for positives, all bits for
+    negatives), the low word 0xFFFFFFFF - index."""
+    hi = (keys >> np.uint64(32)).astype(np.uint32)
+    lo = (keys & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    bits = np.where(hi & np.uint32(0x80000000), hi ^ np.uint32(0x80000000), ~hi)
+    return bits.view(np.float32), (np.uint32(0xFFFFFFFF) - lo).astype(np.int64)
+
+
+@pytest.mark.parametrize("bf16,V", [(True, 151936), (False, 50000)], ids=["bf16_V151936", "f32_V50000"])
+def test_chunk_scores_match_oracle(bf16, V):
+    """Each chunk's best (score, index) as the first launch leaves it in the
+    workspace, against the oracle's float32 scores: the index holds the
+    chunk's best oracle score (up to a near tie) and the score agrees with the
+    oracle's at that index within 8 units in the last place of max(|score|,
+    16.64), the noise's largest size (two logarithms of about 1 ulp each, a
+    rounded fma and the sum's rounding on either side)."""
+    B = 6
+    g = torch.Generator().manual_seed(77 + V)
+    base = torch.randn(B, V, generator=g) * 3.0
+    base = base.to(torch.bfloat16) if bf16 else base
+    temps = torch.tensor([0.5, 1.0, 1.7, 0.8, 3.0, 0.31], dtype=torch.float32)
+    seeds = torch.randint(-(2 ** 62), 2 ** 62, (B,), generator=g, dtype=torch.int64)
+    offsets = torch.randint(0, 2 ** 40, (B,), generator=g, dtype=torch.int64)
+    ws = torch.zeros(pkv.sample_workspace_size(B, V), dtype=torch.uint8, device=DEV)
+    log(f"chunk scores {'bf16' if bf16 else 'fp32'} B={B} V={V}")
+    pkv.sample_gumbel(base.to(DEV), seeds.to(DEV), temps.to(DEV), offsets.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    C = _CHUNK[bf16]
+    nchunks = -(-V // C)
+    keys = ws[: B * nchunks * 8].view(torch.int64).cpu().numpy().view(np.uint64).reshape(B, nchunks)
+    got_s, got_i = _decode_keys(keys)
+    _, scores = S.sample(base.float().numpy(), temps.numpy(), seeds.numpy(), offsets.numpy())
+    worst = 0.0
+    for b in range(B):
+        s = scores[b]
+        for c in range(nchunks):
+            lo, hi = c * C, min(V, (c + 1) * C)
+            i = int(got_i[b, c])
+            assert lo <= i < hi, f"row {b} chunk {c}: index {i} outside [{lo}, {hi})"
+            ref = float(s[i])
+            ulp = float(np.spacing(np.float32(max(abs(ref), 16.64))))
+            err = abs(float(got_s[b, c]) - ref) / ulp
+            worst = max(worst, err)
+            assert err <= 8.0, f"row {b} chunk {c}: score {got_s[b, c]} vs oracle {ref} ({err:.1f} ulp)"
+            assert ref >= float(s[lo:hi].max()) - 8 * ulp, f"row {b} chunk {c}: not the chunk's best"
+    log(f"chunk scores: {B * nchunks} chunks, worst {worst:.2f} ulp")
