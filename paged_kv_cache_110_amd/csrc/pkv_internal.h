@@ -56,6 +56,10 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
                          const DecodePlan& plan, hipStream_t stream);
 
+// Query tiles of a prefill call (the grid's y extent, at most 65535).
+int64_t prefill_query_tiles(int32_t max_seqlen_q, int32_t G);
+constexpr int64_t kPrefillMaxQueryTiles = 65535;
+
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                           const uint16_t* v_cache, const int32_t* block_tables,
                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t B,

@@ -10,7 +10,11 @@
 // (v_mfma_f32_32x32x16_bf16, bf16 in, fp32 accumulate):
 //  - a workgroup (4 wavefronts) owns one KV head, one sequence and a tile of
 //    query positions; its M dimension packs (query position, head of the
-//    group) pairs, 32 per wavefront, so all G heads share every K/V tile;
+//    group) pairs, 32 per wavefront, so all G heads share every K/V tile.
+//    (8 wavefronts share each tile between twice the rows but run slower:
+//    the per-tile barrier then keeps both wavefronts of a SIMD in the same
+//    phase, while two 4-wavefront workgroups per CU drift apart and overlap
+//    one's softmax with the other's MFMAs);
 //  - K/V tiles of 64 keys are gathered through the block table (one look-up
 //    per tile when a tile lies inside one block, per row otherwise, so any
 //    power-of-two block size works) into LDS, double-buffered, the next tile's
@@ -28,14 +32,21 @@
 //    ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit elements;
 //  - online softmax in the log2 domain with the same lazy rescale as decode;
 //    only tiles that cross the diagonal are masked;
-//  - workgroups run the last (most expensive, causally longest) query tiles
-//    of every sequence first.
+//  - grid (KV head, query tile, sequence), so the dispatch order is sequence
+//    by sequence and, within one, the last (most expensive, causally longest)
+//    query tile first.  Workgroups run on XCD (linear id mod 8), so with 8 KV
+//    heads every XCD serves one head, and the workgroups it runs at a time
+//    are the query tiles of a few sequences, which stream the same K/V tiles
+//    at about the same time: those hit in the XCD's L2.  (Query tile
+//    outermost spread each XCD over every sequence at once and fetched about
+//    16 times the K/V bytes from HBM.)
 #include "device_common.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
-constexpr int kPrefillBN = 64;  // keys per tile
+constexpr int kPrefillBN = 64;     // keys per tile
+constexpr int kPrefillWaves = 4;   // wavefronts per workgroup, 32 packed query rows each
 constexpr float kPrefillLazy = 8.0f;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -77,27 +88,28 @@ __device__ __forceinline__ int swz(int row) {
 // carries total_k, and block_tables, bs_log2 and maxb are unused.  q, k and v
 // rows are q_stride / k_stride / v_stride elements apart (views of a fused
 // projection), heads and d contiguous.
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+template <int D, int G, int NWV, bool PAGED>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, uint16_t* __restrict__ out,
     int32_t total_q, int32_t H_kv, int32_t num_blocks, int32_t bs_log2, int32_t maxb,
     int64_t q_stride, int64_t k_stride, int64_t v_stride, float scale_log2e) {
   constexpr int BN = kPrefillBN;
+  constexpr int NT = 64 * NWV;         // threads per workgroup
   constexpr int QPW = 32 / G;          // query positions per wavefront
-  constexpr int QPB = 4 * QPW;         // query positions per workgroup
+  constexpr int QPB = NWV * QPW;       // query positions per workgroup
   constexpr int KS = D / 16;           // k-steps of S^T = K Q^T
   constexpr int DB = D / 32;           // 32-wide d blocks of O^T
   constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;       // rows per load pass
+  constexpr int RPP = NT / CPR;        // rows per load pass (a multiple of 16)
   constexpr int PASSES = BN / RPP;     // load passes per tile and tensor
   constexpr int TILE = BN * D;         // elements per K (or V) tile
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE];  // [buf][K|V][BN][D]
 
   const int h_kv = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   if (nq <= 0 || nk < nq || qs < 0) return;
   const int c = nk - nq;
   const int nqt = (nq + QPB - 1) / QPB;
-  const int qt = nqt - 1 - (int)blockIdx.z;
+  const int qt = nqt - 1 - (int)blockIdx.y;
   if (qt < 0) return;
   const int q0 = qt * QPB;
   const int kend = min(nk, c + q0 + QPB);
@@ -126,6 +138,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const bool row_ok = qq < nq && (int64_t)qs + qq < total_q;
   const int qpos = c + qq;
   const int wave_first_pos = c + q0 + wave * QPW;
+  const int wave_last_pos = wave_first_pos + QPW - 1;
 
   bf16x8 qf[KS];
   {
@@ -340,7 +353,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     uint16_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
     const bool more = kt + 1 < ntiles;
     if (more) load_tile(kt + 1);
-    compute_tile(kt, cur);
+    // a tile wholly past this wavefront's last position is masked out for all
+    // its rows: it would add nothing, so only the loading is shared
+    if (kt * BN <= wave_last_pos) compute_tile(kt, cur);
     if (more) stash_tile(nxt);
     __syncthreads();
   }
@@ -367,8 +382,8 @@ static void launch_pf(dim3 grid, hipStream_t st, const uint16_t* q, const uint16
                       const uint16_t* vc, const int32_t* bt, const int32_t* cq, const int32_t* ck,
                       uint16_t* out, int32_t total_q, int32_t H_kv, int32_t nb, int32_t bsl,
                       int32_t maxb, int64_t qs, int64_t ks, int64_t vs, float sl2e) {
-  hipLaunchKernelGGL((prefill_kernel<D, G, PAGED>), grid, dim3(256), 0, st, q, kc, vc, bt, cq, ck,
-                     out, total_q, H_kv, nb, bsl, maxb, qs, ks, vs, sl2e);
+  hipLaunchKernelGGL((prefill_kernel<D, G, kPrefillWaves, PAGED>), grid, dim3(64 * kPrefillWaves), 0,
+                     st, q, kc, vc, bt, cq, ck, out, total_q, H_kv, nb, bsl, maxb, qs, ks, vs, sl2e);
 }
 
 template <bool PAGED>
@@ -380,9 +395,8 @@ static hipError_t launch_prefill_any(uint16_t* out, const uint16_t* q, const uin
                                      int32_t maxb, int64_t qs, int64_t ks, int64_t vs,
                                      float softmax_scale, hipStream_t stream) {
   const int G = H_q / H_kv;
-  const int qpb = 4 * (32 / G);
-  const unsigned zt = (unsigned)((max_seqlen_q + qpb - 1) / qpb);
-  dim3 grid((unsigned)H_kv, (unsigned)B, zt);
+  const unsigned zt = (unsigned)prefill_query_tiles(max_seqlen_q, G);
+  dim3 grid((unsigned)H_kv, zt, (unsigned)B);
   const float sl2e = softmax_scale * 1.4426950408889634f;
 #define PKV_PF(DD, GG)                                                                        \
   launch_pf<DD, GG, PAGED>(grid, stream, q, k, v, block_tables, cu_seqlens_q, cu_seqlens_k, out, \
@@ -404,6 +418,11 @@ static hipError_t launch_prefill_any(uint16_t* out, const uint16_t* q, const uin
   }
 #undef PKV_PF
   return hipGetLastError();
+}
+
+int64_t prefill_query_tiles(int32_t max_seqlen_q, int32_t G) {
+  const int64_t qpb = kPrefillWaves * (32 / G);
+  return ((int64_t)max_seqlen_q + qpb - 1) / qpb;
 }
 
 static int ilog2p(int x) {

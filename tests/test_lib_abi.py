@@ -90,6 +90,10 @@ def test_attention_argument_checks_before_launch():
 
     assert pf(H_q=6, H_kv=4) == 1
     assert pf(d=256) == 2
+    # more query tiles (of 128 / G positions) than the grid's 65535
+    too_many = 65535 * 64 + 1
+    assert lib.pkv_prefill_varlen(p, p, p, p, p, p, p, 2, 10, too_many, 10, 4, 2, 64, 8, 16, 3,
+                                  0.125, None) == 2
     assert lib.pkv_prefill_varlen(p, p, p, p, p, p, p, 0, 0, 0, 0, 4, 2, 64, 8, 16, 3, 0.125,
                                   None) == 0  # nothing to do
 
@@ -113,6 +117,7 @@ def test_packed_prefill_argument_checks_before_launch():
     assert pk(B=-1) == 1
     assert pk(d=96, qs=768, ks=384, vs=384) == 2
     assert pk(H_q=64, H_kv=4, qs=4096) == 2  # group of 16
+    assert pk(mq=65535 * 128 // 2 + 1) == 2  # more than 65535 query tiles (G = 2)
 
 
 def test_workspace_size_formula():
