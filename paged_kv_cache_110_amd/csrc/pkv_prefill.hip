@@ -14,7 +14,8 @@
 //    (8 wavefronts share each tile between twice the rows but run slower:
 //    the per-tile barrier then keeps both wavefronts of a SIMD in the same
 //    phase, while two 4-wavefront workgroups per CU drift apart and overlap
-//    one's softmax with the other's MFMAs);
+//    one's softmax with the other's MFMAs.  Two groups of 4 run half a tile
+//    apart with a barrier per half tile ran slower still);
 //  - K/V tiles of 64 keys are gathered through the block table (one look-up
 //    per tile when a tile lies inside one block, per row otherwise, so any
 //    power-of-two block size works) into LDS, double-buffered, the next tile's
@@ -39,7 +40,7 @@
 //    are the query tiles of a few sequences, which stream the same K/V tiles
 //    at about the same time: those hit in the XCD's L2.  (Query tile
 //    outermost spread each XCD over every sequence at once and fetched about
-//    16 times the K/V bytes from HBM.)
+//    13 times the K/V bytes from HBM.)
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -146,6 +147,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = row_ok ? ld16(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      // wait for q here, once: otherwise the wait-count pass cannot tell
+      // inside the tile loop that these loads are done, and makes the first
+      // score MFMA of every tile wait for the next tile's K/V loads as well
+      asm volatile("" : "+v"(v));
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -172,14 +177,16 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
   // V^T operand reads: rows kb * 32 + 16 * s2 + rlo (+ 8), 4 columns at col
   const int i16 = lane & 15;
   const int grp16 = lane >> 4;
-  int voff[DB][2];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int col = db * 32 + 16 * (grp16 & 1) + 4 * (i16 & 3);
+  // d block db's chunk is block 0's chunk XOR 4 * db (the swizzle changes
+  // only a row's low chunk bits within each group of four), so its offset is
+  // voff[hi] ^ (32 * db)
+  int voff[2];
+  {
+    const int col = 16 * (grp16 & 1) + 4 * (i16 & 3);
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
       const int rlo = 4 * half + (i16 >> 2) + 8 * hi;
-      voff[db][hi] = rlo * D + (((col >> 3) ^ swz<CPR>(rlo)) << 3) + (col & 7);
+      voff[hi] = rlo * D + (((col >> 3) ^ swz<CPR>(rlo)) << 3) + (col & 7);
     }
   }
   const uint16_t* khead = k_cache + (int64_t)h_kv * D;
@@ -257,8 +264,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
       full_next = false;
     }
   };
-  auto stash_tile = [&](uint16_t* kt_lds) {
-    uint16_t* vt_lds = kt_lds + TILE;
+  auto stash_tile = [&](uint16_t* kt_lds, uint16_t* vt_lds) {
     if (full_next) {
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
@@ -276,10 +282,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
     }
   };
 
-  // One 64-key tile from LDS buffer BUF: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto compute_tile = [&](int kt, const uint16_t* kt_lds) {
-    const uint16_t* vt_lds = kt_lds + TILE;
-    f32x16 sacc[2];
+  // One 64-key tile in three parts: S^T = K Q^T (MFMA), the online softmax
+  // (VALU; produces P in fp16), O^T += V^T P^T (MFMA).
+  auto score_mfma = [&](const uint16_t* kt_lds, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
@@ -291,6 +296,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
                                                            sacc[kb], 0, 0, 0);
       }
     }
+  };
+  auto softmax = [&](int kt, f32x16 (&sacc)[2], f16x8 (&pf)[2][2]) {
     // causal mask, only on tiles that reach past this wavefront's first position
     if (kt * BN + BN - 1 > wave_first_pos) {
 #pragma unroll
@@ -318,7 +325,6 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
     }
     // P = 2^(s * scale * log2 e - m) (at most 2^8 with the lazy rescale),
     // rounded to fp16 for the PV product
-    f16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -329,6 +335,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
           l += p;
           pf[kb][s2][e] = (_Float16)p;
         }
+  };
+  auto pv_mfma = [&](const uint16_t* vt_lds, const f16x8 (&pf)[2][2]) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -336,8 +344,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int rofs = (kb * 32 + 16 * s2) * D;
-          const i16x4 va = lds_read_tr16(vt_lds + voff[db][0] + rofs);
-          const i16x4 vb = lds_read_tr16(vt_lds + voff[db][1] + rofs);
+          const i16x4 va = lds_read_tr16(vt_lds + (voff[0] ^ (32 * db)) + rofs);
+          const i16x4 vb = lds_read_tr16(vt_lds + (voff[1] ^ (32 * db)) + rofs);
           typedef short i16x8 __attribute__((ext_vector_type(8)));
           const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, v8),
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
   };
 
   load_tile(0);
-  stash_tile(lds);
+  stash_tile(lds, lds + TILE);
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
     uint16_t* cur = lds + (kt & 1) * 2 * TILE;
@@ -355,8 +363,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
     if (more) load_tile(kt + 1);
     // a tile wholly past this wavefront's last position is masked out for all
     // its rows: it would add nothing, so only the loading is shared
-    if (kt * BN <= wave_last_pos) compute_tile(kt, cur);
-    if (more) stash_tile(nxt);
+    if (kt * BN <= wave_last_pos) {
+      f32x16 sacc[2];
+      f16x8 pf[2][2];
+      score_mfma(cur, sacc);
+      softmax(kt, sacc, pf);
+      pv_mfma(cur + TILE, pf);
+    }
+    if (more) stash_tile(nxt, nxt + TILE);
     __syncthreads();
   }
 
