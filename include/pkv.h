@@ -259,12 +259,13 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
  *   temperatures device [B] fp32, or null for T = 1
  *   seeds        device [B] int64;  offsets: device [B] int64, or null for 0
  *   tokens       device [B] int64, written
- *   workspace    device, pkv_sample_workspace_size(B, V) bytes (no contents
- *                carried between calls)
+ *   workspace    device, pkv_sample_workspace_size(B, V) bytes, 8-byte
+ *                aligned (no contents carried between calls; calls that
+ *                share one must run in stream order, never concurrently)
  * Logits must be finite (NaN and infinities are unspecified).
  * PKV_EINVAL: B < 0, B > 65535, V < 1, row_stride < V or not a multiple of
- * 8 (bf16) / 4 (fp32), null pointers or misaligned logits (B > 0), a short
- * workspace.
+ * 8 (bf16) / 4 (fp32), null pointers, misaligned logits or workspace
+ * (B > 0), a short workspace.
  * B == 0 enqueues nothing.
  */
 /* Workspace bytes pkv_sample_gumbel needs: 8 per row per 4096-logit chunk

@@ -312,6 +312,7 @@ pkv_status pkv_sample_gumbel(int64_t* tokens, const void* logits, int32_t logits
   if (row_stride % (logits_bf16 ? 8 : 4) != 0) return PKV_EINVAL;
   if (B == 0) return PKV_OK;
   if (!tokens || !logits || !seeds || !workspace || !aligned16(logits)) return PKV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 8 != 0) return PKV_EINVAL;  // 64-bit chunk keys
   if (B > 65535) return PKV_EINVAL;  // one grid row per batch row
   if (workspace_bytes < pkv_sample_workspace_size(B, V)) return PKV_EINVAL;
   return launch_status(pkv::launch_sample(tokens, logits, logits_bf16 != 0, row_stride, B, V,

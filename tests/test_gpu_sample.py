@@ -167,3 +167,24 @@ def test_chunk_scores_match_oracle(bf16, V):
             assert err <= 8.0, f"row {b} chunk {c}: score {got_s[b, c]} vs oracle {ref} ({err:.1f} ulp)"
             assert ref >= float(s[lo:hi].max()) - 8 * ulp, f"row {b} chunk {c}: not the chunk's best"
     log(f"chunk scores: {B * nchunks} chunks, worst {worst:.2f} ulp")
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves calls of different shapes in stream order, its
+    contents left by the previous call: every call matches the oracle."""
+    shapes = [(8, 151936, True), (3, 5000, False), (8, 151936, True), (1, 9000, True)]
+    Bmax, Vmax = 8, 151936
+    ws = torch.full((pkv.sample_workspace_size(Bmax, Vmax),), 0xA5, dtype=torch.uint8, device=DEV)
+    for n, (B, V, bf16) in enumerate(shapes):
+        g = torch.Generator().manual_seed(500 + n)
+        base = torch.randn(B, V, generator=g) * 3.0
+        base = base.to(torch.bfloat16) if bf16 else base
+        temps = torch.rand(B, generator=g) + 0.5
+        seeds = torch.randint(0, 2 ** 62, (B,), generator=g, dtype=torch.int64)
+        offsets = torch.randint(0, 2 ** 30, (B,), generator=g, dtype=torch.int64)
+        log(f"reuse call {n}: B={B} V={V} {'bf16' if bf16 else 'fp32'}")
+        tok = pkv.sample_gumbel(base.to(DEV), seeds.to(DEV), temps.to(DEV), offsets.to(DEV),
+                                workspace=ws)
+        torch.cuda.synchronize()
+        _check(tok, base.float().numpy(), temps.numpy(), seeds.numpy(), offsets.numpy(),
+               f"reuse call {n}")

@@ -318,6 +318,7 @@ def test_sample_argument_checks_before_any_hip_call():
     assert call(a, a + 2, 1, 104, 2, 100, None, a, None, a, 4096, None) == 1     # misaligned
     assert call(a, a, 1, 104, 2, 100, None, None, None, a, 4096, None) == 1      # no seeds
     assert call(a, a, 1, 104, 2, 100, None, a, None, a, 8, None) == 1            # short workspace
+    assert call(a, a, 1, 104, 2, 100, None, a, None, a + 4, 4096, None) == 1     # workspace % 8
     assert lib.pkv_sample_workspace_size(2, 100) == 16
     assert lib.pkv_sample_workspace_size(3, 151936) == 3 * 38 * 8
     assert lib.pkv_sample_workspace_size(0, 10) == 0
