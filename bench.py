@@ -377,7 +377,7 @@ def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
 
 
 SECONDARY = ("packed_prefill", "graph_decode", "device_metadata", "gumbel_sample",
-             "long_decode", "prefix_prefill", "full_step")
+             "long_decode", "prefix_prefill", "full_step", "wide_gqa_decode")
 
 
 def main() -> int:
@@ -386,7 +386,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3_decode",
-                    choices=["qwen3_decode", "long_decode", "prefix_prefill", "full_step"])
+                    choices=["qwen3_decode", "long_decode", "prefix_prefill", "full_step",
+                             "wide_gqa_decode"])
     ap.add_argument("--pools", type=int, default=2,
                     help="independent copies of the cache rotated across steps (single-layer workloads)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -463,7 +464,7 @@ def main() -> int:
             secondary["device_metadata"] = run_meta(n2, 3, torch, pkv, log)
         if "gumbel_sample" in wanted:
             secondary["gumbel_sample"] = run_sample(n2, 3, torch, pkv, log)
-        for name in ["long_decode", "prefix_prefill", "full_step"]:
+        for name in ["long_decode", "prefix_prefill", "full_step", "wide_gqa_decode"]:
             if name == args.workload or name not in wanted:
                 continue
             r = run_workload(name, max(5, args.steps // 2), 2,

@@ -31,6 +31,14 @@
 //    weight), so the compiler's wait counts track the ring exactly;
 //  - q.k uses v_dot2_f32_bf16 on packed bf16 pairs (exact products, fp32
 //    sums), reduced across the LPT lanes of a token with DPP;
+//  - wide groups (G >= 4) take the MFMA form instead (MF): the VALU's q.k and
+//    p.v work per byte of K/V grows with G (about 80 instructions per tile
+//    and query head) and at G = 8 would outrun the HBM stream.  Each tile is
+//    staged in LDS (swizzled 16-byte chunks), S^T = K Q^T runs on
+//    v_mfma_f32_16x16x32_bf16 (16 keys x the G heads padded to 16 columns),
+//    the online softmax on the four scores a lane holds, and O^T += V^T P^T
+//    on v_mfma_f32_16x16x16_bf16 with V^T read transposed from LDS
+//    (ds_read_b64_tr_b16) and P as bf16 high and low parts;
 //  - online softmax (ascendai overview, "FlashAttention 集成": running max and
 //    sum, rescaled output) per lane group, in the log2 domain with
 //    scale*log2(e) folded in; the rescale is lazy (only when some lane's tile
@@ -75,7 +83,7 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 // Unit counts fit in int32: the host rejects shapes where
 // B * H_kv * ceil(max_blocks_per_seq * block_size / 16) could exceed INT32_MAX.
-template <int D, int G, int EPL, int NBUF, int WPE>
+template <int D, int G, int EPL, int NBUF, int WPE, bool MF>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -88,9 +96,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   constexpr int TPL = kDecodeTile / TPI; // tokens per lane per tile
   constexpr int NW = EPL / 8;            // 128-bit words per lane per row
   static_assert(TPI * TPL == kDecodeTile, "tile shape");
+  static_assert(!MF || (NW == 1 && G <= 16), "MFMA form: one 128-bit word per lane and row");
 
   __shared__ int pre[kSeqCache + 1];  // units of the sequences before b
   __shared__ int lenc[kSeqCache];     // clamped context length of b
+  // MFMA form: the tile being computed, K then V, 16 rows of D bf16 each with
+  // swizzled 16-byte chunks (mf_off)
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[MF ? 2 * kDecodeTile * D : 8];
 
   const int lane = threadIdx.x;
   const int grp = lane / LPT;
@@ -277,19 +289,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   // buffers cover the NBUF - 1 tiles between the cursors even for one-tile
   // pieces; if both are taken the piece loads its q when it starts.
   constexpr int kQBufs = NBUF > 2 ? 2 : 1;
-  uint32_t qn0[G][EPL / 2], qn1[G][EPL / 2];
+  // VALU form: lane-group layout, q[g] words of this lane's d chunk.  MFMA
+  // form (QM): the B operand of the score MFMA, column mcol = head mcol of
+  // the group (zero past G), d = 32 * ks + 8 * mq .. + 7 for k-step ks.
+  constexpr int KSM = D / 32;  // k-steps of the score MFMA
+  constexpr int DBM = D / 16;  // 16-row d blocks of O^T
+  const int mcol = lane & 15;
+  const int mq = lane >> 4;
+  struct QV { uint32_t w[G][EPL / 2]; };
+  struct QM { u32x4 k[KSM]; };
+  using QBuf = typename std::conditional<MF, QM, QV>::type;
+  QBuf qn0, qn1;
   int qn_seg0 = -1, qn_seg1 = -1;  // (sequence, KV head) index held, -1 = free
-  auto load_q = [&](int b, int h, uint32_t (&dst)[G][EPL / 2]) {
+  auto load_q = [&](int b, int h, QBuf& dst) {
     const int64_t head0 = (int64_t)b * H_q + (int64_t)h * G;
+    if constexpr (MF) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+      for (int ks = 0; ks < KSM; ++ks)
+        dst.k[ks] = mcol < G ? ld16(q + (head0 + mcol) * D + 32 * ks + 8 * mq) : u32x4{0, 0, 0, 0};
+    } else {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const u32x4 v = ld16(q + (head0 + g) * D + dofs(w));
-        dst[g][4 * w + 0] = v[0];
-        dst[g][4 * w + 1] = v[1];
-        dst[g][4 * w + 2] = v[2];
-        dst[g][4 * w + 3] = v[3];
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const u32x4 v = ld16(q + (head0 + g) * D + dofs(w));
+          dst.w[g][4 * w + 0] = v[0];
+          dst.w[g][4 * w + 1] = v[1];
+          dst.w[g][4 * w + 2] = v[2];
+          dst.w[g][4 * w + 3] = v[3];
+        }
       }
     }
   };
@@ -382,160 +410,290 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     pin(L);
   };
 
-  uint32_t qw[G][EPL / 2];
-  float acc[G][EPL];
-  float m[G], l[G];
+  QBuf qw;
+  // VALU form: per lane group, G running (m, l) and acc[g][EPL] of this
+  // lane's d chunk.  MFMA form: O^T in d blocks (lane: rows d = 16 * db +
+  // 4 * mq .. + 3 of column mcol), one (m, l) per lane for column mcol
+  // (m common to the column's four lanes, l a partial sum over its keys).
+  float acc[MF ? 1 : G][EPL];
+  float m[MF ? 1 : G], l[MF ? 1 : G];
+  f32x4 om[MF ? DBM : 1];
+
+  auto pin_q = [&](QBuf& x) {
+    if constexpr (MF) {
+#pragma unroll
+      for (int ks = 0; ks < KSM; ++ks) asm volatile("" : "+v"(x.k[ks]));
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < EPL / 2; ++k) asm volatile("" : "+v"(x.w[g][k]));
+    }
+  };
 
   auto begin_segment = [&](const Meta& mt) {
     const int id = mt.b * H_kv + mt.h;
     if (qn_seg0 == id) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) qw[g][k] = qn0[g][k];
+      qw = qn0;
       qn_seg0 = -1;
     } else if (kQBufs > 1 && qn_seg1 == id) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) qw[g][k] = qn1[g][k];
+      qw = qn1;
       qn_seg1 = -1;
     } else {
       // Rare (both prefetch buffers taken): load q now and wait for it here,
       // so that qw carries no pending load out of this branch (otherwise the
       // first use of qw on every path would wait for this step's tile loads).
       load_q(mt.b, mt.h, qw);
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int k = 0; k < EPL / 2; ++k) asm volatile("" : "+v"(qw[g][k]));
+      pin_q(qw);
     }
+    if constexpr (MF) {
+      m[0] = kNegSentinel;
+      l[0] = 0.f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = kNegSentinel;
-      l[g] = 0.f;
+      for (int db = 0; db < DBM; ++db) om[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+      for (int g = 0; g < G; ++g) {
+        m[g] = kNegSentinel;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+      }
+    }
+  };
+
+  // MFMA form: element offset of 16-byte chunk c of row r (0..15) of a staged
+  // K or V tile.  The XOR keeps the chunk stores (16 lanes per row), the K
+  // operand reads (16 rows, one chunk) and the transposing V reads (8 rows x
+  // 2 chunks per 32 lanes) free of LDS bank conflicts.
+  auto mf_off = [&](int r, int c) {
+    const int sw = D == 128 ? 2 * (r & 7) + (r >> 3) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    return r * D + ((c ^ sw) << 3);
+  };
+
+  // MFMA form of one tile: stage K and V in LDS, S^T = K Q^T (16 keys x 16
+  // columns, one v_mfma_f32_16x16x32_bf16 per 32 d), the online softmax on
+  // the four scores each lane holds (keys 4 * mq .. + 3 of column mcol), then
+  // O^T += V^T P^T per 16-row d block with V^T read transposed from LDS
+  // (ds_read_b64_tr_b16) and P split into bf16 high and low parts (two
+  // v_mfma_f32_16x16x16_bf16), which keeps P to about 2^-16.
+  auto compute_tile_mf = [&](const u32x4 (&kx)[TPL][NW], const u32x4 (&vx)[TPL][NW], int rows) {
+    if constexpr (MF) {
+      uint16_t* kl = kv_lds;
+      uint16_t* vl = kv_lds + kDecodeTile * D;
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        const int r = grp + i * TPI;
+        *reinterpret_cast<u32x4*>(kl + mf_off(r, sub)) = kx[i][0];
+        *reinterpret_cast<u32x4*>(vl + mf_off(r, sub)) = vx[i][0];
+      }
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSM; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + mf_off(mcol, 4 * ks + mq));
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                     __builtin_bit_cast(bf16x8, qw.k[ks]), st, 0, 0, 0);
+      }
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = 4 * mq + r < rows ? st[r] * scale_log2e : -INFINITY;
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = cross_reduce<16, true>(mx);
+      if (__any(mx > m[0] + kLazyRescale)) {
+        const float mn = fmaxf(m[0], mx);
+        const float alpha = fast_exp2(m[0] - mn);
+        m[0] = mn;
+        l[0] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBM; ++db) om[db] *= alpha;
+      }
+      i16x4 ph, pl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(sc[r] - m[0]);
+        l[0] += p;
+        const __bf16 hi = (__bf16)p;
+        const __bf16 lo = (__bf16)(p - (float)hi);
+        ph[r] = __builtin_bit_cast(short, hi);
+        pl[r] = __builtin_bit_cast(short, lo);
+      }
+#pragma unroll
+      for (int db = 0; db < DBM; ++db) {
+        // lane mcol of quarter mq gets V[4 * mq + e][16 * db + mcol], e = 0..3
+        const int col = 16 * db + 4 * (mcol & 3);
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vl + mf_off(4 * mq + (mcol >> 2), col >> 3) +
+                                                       (col & 7)));
+        om[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, om[db], 0, 0, 0);
+        om[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, om[db], 0, 0, 0);
+      }
     }
   };
 
   auto compute_tile = [&](const u32x4 (&kx)[TPL][NW], const u32x4 (&vx)[TPL][NW], int rows) {
-    // scores in the log2 domain
-    float sc[TPL][G];
+    if constexpr (MF) {
+      compute_tile_mf(kx, vx, rows);
+      return;
+    } else {
+      // scores in the log2 domain
+      float sc[TPL][G];
 #pragma unroll
-    for (int i = 0; i < TPL; ++i) {
+      for (int i = 0; i < TPL; ++i) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float dsum = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            dsum = dot2_bf16(qw.w[g][4 * w + 0], kx[i][w][0], dsum);
+            dsum = dot2_bf16(qw.w[g][4 * w + 1], kx[i][w][1], dsum);
+            dsum = dot2_bf16(qw.w[g][4 * w + 2], kx[i][w][2], dsum);
+            dsum = dot2_bf16(qw.w[g][4 * w + 3], kx[i][w][3], dsum);
+          }
+          dsum = group_sum<LPT>(dsum);
+          sc[i][g] = grp + i * TPI < rows ? dsum * scale_log2e : -INFINITY;
+        }
+      }
+      // lazy running-max update
+      bool need = false;
+      float mt[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float dsum = 0.f;
+        mt[g] = sc[0][g];
+#pragma unroll
+        for (int i = 1; i < TPL; ++i) mt[g] = fmaxf(mt[g], sc[i][g]);
+        need |= mt[g] > m[g] + kLazyRescale;
+      }
+      if (__any(need)) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float mn = fmaxf(m[g], mt[g]);
+          const float alpha = fast_exp2(m[g] - mn);
+          m[g] = mn;
+          l[g] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+        }
+      }
+      // weights and weighted V
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        float p[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          p[g] = fast_exp2(sc[i][g] - m[g]);
+          l[g] += p[g];
+        }
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          dsum = dot2_bf16(qw[g][4 * w + 0], kx[i][w][0], dsum);
-          dsum = dot2_bf16(qw[g][4 * w + 1], kx[i][w][1], dsum);
-          dsum = dot2_bf16(qw[g][4 * w + 2], kx[i][w][2], dsum);
-          dsum = dot2_bf16(qw[g][4 * w + 3], kx[i][w][3], dsum);
-        }
-        dsum = group_sum<LPT>(dsum);
-        sc[i][g] = grp + i * TPI < rows ? dsum * scale_log2e : -INFINITY;
-      }
-    }
-    // lazy running-max update
-    bool need = false;
-    float mt[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      mt[g] = sc[0][g];
+          for (int k = 0; k < 4; ++k) {
+            const float v0 = bf16_lo(vx[i][w][k]);
+            const float v1 = bf16_hi(vx[i][w][k]);
 #pragma unroll
-      for (int i = 1; i < TPL; ++i) mt[g] = fmaxf(mt[g], sc[i][g]);
-      need |= mt[g] > m[g] + kLazyRescale;
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mn = fmaxf(m[g], mt[g]);
-        const float alpha = fast_exp2(m[g] - mn);
-        m[g] = mn;
-        l[g] *= alpha;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
-      }
-    }
-    // weights and weighted V
-#pragma unroll
-    for (int i = 0; i < TPL; ++i) {
-      float p[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        p[g] = fast_exp2(sc[i][g] - m[g]);
-        l[g] += p[g];
-      }
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float v0 = bf16_lo(vx[i][w][k]);
-          const float v1 = bf16_hi(vx[i][w][k]);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            acc[g][8 * w + 2 * k] += p[g] * v0;
-            acc[g][8 * w + 2 * k + 1] += p[g] * v1;
+            for (int g = 0; g < G; ++g) {
+              acc[g][8 * w + 2 * k] += p[g] * v0;
+              acc[g][8 * w + 2 * k + 1] += p[g] * v1;
+            }
           }
         }
+      }
+
+    }
+  };
+
+  // MFMA form of the end of a piece: the column's l summed over its four
+  // lanes (m is already common to them); lanes of columns below G hold d rows
+  // 16 * db + 4 * mq .. + 3 of head mcol, written as bf16 (a segment in one
+  // piece) or as an fp32 partial with (m, l) (a piece of a cut segment).
+  auto end_segment_mf = [&](const Meta& mt) {
+    if constexpr (MF) {
+      const float lt = cross_reduce<16, false>(l[0]);
+      const bool first_piece = !(mt.flags & kBeganBefore);
+      const bool last_piece = (mt.flags & kSegEnd) != 0;
+      if (lane == 0) {
+        int32_t* rec = reinterpret_cast<int32_t*>(ws_seg + ((int64_t)mt.b * H_kv + mt.h));
+        if (first_piece) rec[0] = mt.k;
+        if (last_piece) rec[1] = mt.k;
+      }
+      if (mcol >= G) return;
+      const int64_t head0 = (int64_t)mt.b * H_q + (int64_t)mt.h * G;
+      if (first_piece && last_piece) {
+        const float inv = 1.0f / lt;
+        uint16_t* op = out + (head0 + mcol) * D + 4 * mq;
+#pragma unroll
+        for (int db = 0; db < DBM; ++db)
+          *reinterpret_cast<u32x2*>(op + 16 * db) =
+              u32x2{pack_bf16x2(om[db][0] * inv, om[db][1] * inv),
+                    pack_bf16x2(om[db][2] * inv, om[db][3] * inv)};
+      } else {
+        const int slot = first_piece ? 1 : 0;
+        const int64_t row = ((int64_t)mt.k * 2 + slot) * G + mcol;
+        float* ap = ws_acc + row * D + 4 * mq;
+#pragma unroll
+        for (int db = 0; db < DBM; ++db) *reinterpret_cast<f32x4*>(ap + 16 * db) = om[db];
+        if (mq == 0) *reinterpret_cast<float2*>(ws_ml + row * 2) = make_float2(m[0], lt);
       }
     }
   };
 
   auto end_segment = [&](const Meta& mt) {
-    // merge the TPI lane groups (log-sum-exp); group 0 holds the result
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float M = cross_reduce<LPT, true>(m[g]);
-      const float alpha = fast_exp2(m[g] - M);
-      l[g] = cross_reduce<LPT, false>(l[g] * alpha);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = cross_reduce<LPT, false>(acc[g][e] * alpha);
-      m[g] = M;
-    }
-    // A segment in one piece is written directly.  Otherwise its first
-    // piece records its share in k_first and its last piece in k_last; the
-    // merge combines shares k_first .. k_last.
-    const bool first_piece = !(mt.flags & kBeganBefore);
-    const bool last_piece = (mt.flags & kSegEnd) != 0;
-    if (lane == 0) {
-      int32_t* rec = reinterpret_cast<int32_t*>(ws_seg + ((int64_t)mt.b * H_kv + mt.h));
-      if (first_piece) rec[0] = mt.k;
-      if (last_piece) rec[1] = mt.k;
-    }
-    const int64_t head0 = (int64_t)mt.b * H_q + (int64_t)mt.h * G;
-    if (first_piece && last_piece) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float inv = 1.0f / l[g];
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          u32x4 o;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            o[k] = pack_bf16x2(acc[g][8 * w + 2 * k] * inv, acc[g][8 * w + 2 * k + 1] * inv);
-          st16(out + (head0 + g) * D + dofs(w), o);
-        }
-      }
+    if constexpr (MF) {
+      end_segment_mf(mt);
+      return;
     } else {
-      // partial slot 0: the share's piece that began in an earlier share;
-      // slot 1: a piece that begins in this share and goes on past it
-      const int slot = first_piece ? 1 : 0;
+      // merge the TPI lane groups (log-sum-exp); group 0 holds the result
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int64_t row = ((int64_t)mt.k * 2 + slot) * G + g;
-        float* ap = ws_acc + row * D;
+        const float M = cross_reduce<LPT, true>(m[g]);
+        const float alpha = fast_exp2(m[g] - M);
+        l[g] = cross_reduce<LPT, false>(l[g] * alpha);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          *reinterpret_cast<f32x4*>(ap + dofs(w)) =
-              f32x4{acc[g][8 * w], acc[g][8 * w + 1], acc[g][8 * w + 2], acc[g][8 * w + 3]};
-          *reinterpret_cast<f32x4*>(ap + dofs(w) + 4) =
-              f32x4{acc[g][8 * w + 4], acc[g][8 * w + 5], acc[g][8 * w + 6], acc[g][8 * w + 7]};
-        }
-        if (sub == 0) *reinterpret_cast<float2*>(ws_ml + row * 2) = make_float2(m[g], l[g]);
+        for (int e = 0; e < EPL; ++e) acc[g][e] = cross_reduce<LPT, false>(acc[g][e] * alpha);
+        m[g] = M;
       }
+      // A segment in one piece is written directly.  Otherwise its first
+      // piece records its share in k_first and its last piece in k_last; the
+      // merge combines shares k_first .. k_last.
+      const bool first_piece = !(mt.flags & kBeganBefore);
+      const bool last_piece = (mt.flags & kSegEnd) != 0;
+      if (lane == 0) {
+        int32_t* rec = reinterpret_cast<int32_t*>(ws_seg + ((int64_t)mt.b * H_kv + mt.h));
+        if (first_piece) rec[0] = mt.k;
+        if (last_piece) rec[1] = mt.k;
+      }
+      const int64_t head0 = (int64_t)mt.b * H_q + (int64_t)mt.h * G;
+      if (first_piece && last_piece) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float inv = 1.0f / l[g];
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              o[k] = pack_bf16x2(acc[g][8 * w + 2 * k] * inv, acc[g][8 * w + 2 * k + 1] * inv);
+            st16(out + (head0 + g) * D + dofs(w), o);
+          }
+        }
+      } else {
+        // partial slot 0: the share's piece that began in an earlier share;
+        // slot 1: a piece that begins in this share and goes on past it
+        const int slot = first_piece ? 1 : 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int64_t row = ((int64_t)mt.k * 2 + slot) * G + g;
+          float* ap = ws_acc + row * D;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            *reinterpret_cast<f32x4*>(ap + dofs(w)) =
+                f32x4{acc[g][8 * w], acc[g][8 * w + 1], acc[g][8 * w + 2], acc[g][8 * w + 3]};
+            *reinterpret_cast<f32x4*>(ap + dofs(w) + 4) =
+                f32x4{acc[g][8 * w + 4], acc[g][8 * w + 5], acc[g][8 * w + 6], acc[g][8 * w + 7]};
+          }
+          if (sub == 0) *reinterpret_cast<float2*>(ws_ml + row * 2) = make_float2(m[g], l[g]);
+        }
+      }
+
     }
   };
 
@@ -696,7 +854,7 @@ static int ilog2(int x) {
 
 // One wavefront per resident slot of the current device (cached per device
 // and kernel variant).
-template <int D, int G, int EPL, int NBUF, int WPE>
+template <int D, int G, int EPL, int NBUF, int WPE, bool MF>
 static int resident_waves() {
   static int cached[64] = {0};
   int dev = 0;
@@ -706,7 +864,7 @@ static int resident_waves() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, EPL, NBUF, WPE>, 64,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, EPL, NBUF, WPE, MF>, 64,
                                                      0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 8;
@@ -715,22 +873,24 @@ static int resident_waves() {
   return cached[dev];
 }
 
-// Kernel variant per (d, G): elements per lane and ring depth.
+// Kernel variant per (d, G): elements per lane, ring depth, wavefronts per
+// SIMD, and the MFMA form for wide groups (G >= 4), where the VALU's q.k and
+// p.v work per byte of K/V would outrun the HBM stream.
 template <typename F>
 static bool dispatch(int d, int G, F& f) {
   if (d == 128) {
     switch (G) {
-      case 1: f.template run<128, 1, 16, 3, 2>(); return true;
-      case 2: f.template run<128, 2, 16, 3, 2>(); return true;
-      case 4: f.template run<128, 4, 8, 3, 2>(); return true;
-      case 8: f.template run<128, 8, 8, 2, 1>(); return true;
+      case 1: f.template run<128, 1, 16, 3, 2, false>(); return true;
+      case 2: f.template run<128, 2, 16, 3, 2, false>(); return true;
+      case 4: f.template run<128, 4, 8, 3, 2, true>(); return true;
+      case 8: f.template run<128, 8, 8, 3, 2, true>(); return true;
     }
   } else if (d == 64) {
     switch (G) {
-      case 1: f.template run<64, 1, 8, 3, 2>(); return true;
-      case 2: f.template run<64, 2, 8, 3, 2>(); return true;
-      case 4: f.template run<64, 4, 8, 3, 2>(); return true;
-      case 8: f.template run<64, 8, 8, 2, 1>(); return true;
+      case 1: f.template run<64, 1, 8, 3, 2, false>(); return true;
+      case 2: f.template run<64, 2, 8, 3, 2, false>(); return true;
+      case 4: f.template run<64, 4, 8, 3, 2, true>(); return true;
+      case 8: f.template run<64, 8, 8, 3, 2, true>(); return true;
     }
   }
   return false;
@@ -738,8 +898,8 @@ static bool dispatch(int d, int G, F& f) {
 
 struct WaveQuery {
   int waves = 0;
-  template <int D, int G, int EPL, int NBUF, int WPE>
-  void run() { waves = resident_waves<D, G, EPL, NBUF, WPE>(); }
+  template <int D, int G, int EPL, int NBUF, int WPE, bool MF>
+  void run() { waves = resident_waves<D, G, EPL, NBUF, WPE, MF>(); }
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -786,9 +946,9 @@ struct DecodeLaunch {
   int32_t* queue;
   int32_t B, H_kv, nb, bsl, maxb;
   float sl2e;
-  template <int D, int G, int EPL, int NBUF, int WPE>
+  template <int D, int G, int EPL, int NBUF, int WPE, bool MF>
   void run() {
-    hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF, WPE>), grid, dim3(64), 0, st, q, kc, vc, bt, cl,
+    hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF, WPE, MF>), grid, dim3(64), 0, st, q, kc, vc, bt, cl,
                        out, wa, wm, wseg, queue, B, H_kv, nb, bsl, maxb, sl2e);
   }
 };

@@ -180,7 +180,8 @@ def _check_decode_sample(plan, host, meta_full, out, layer, idx, what):
     assert_close(out[idx], ref, what)
 
 
-@pytest.mark.parametrize("name,nsample", [("qwen3_decode", 48), ("long_decode", 6)])
+@pytest.mark.parametrize("name,nsample", [("qwen3_decode", 48), ("long_decode", 6),
+                                          ("wide_gqa_decode", 24)])
 def test_full_size_decode(name, nsample):
     log(f"full-size {name}")
     plan = make_plan(name)

@@ -1,8 +1,11 @@
-"""The five workload shapes of the paged-KV attention path.
+"""The workload shapes of the paged-KV attention path.
 
 Shapes follow the pages' statement of the problem (nano-vllm's decode and
 prefill calls, the 256-token block of its block manager, Qwen3-0.6B-like head
-counts) and the length mixes given for each workload below.
+counts) and the length mixes given for each workload below.  The last one,
+wide_gqa_decode, keeps qwen3_decode's sequences but groups 8 query heads per KV
+head (Qwen3-32B's 64 / 8 / 128 attention), the case the decode kernel's MFMA
+form is for.
 """
 
 # name -> description of the sequence population and head geometry.
@@ -34,9 +37,14 @@ CONFIGS = {
         kind="decode", B=512, lens=("loguniform", 16, 16384), block_size=256,
         H_q=32, H_kv=8, d=128, layers=28,
     ),
+    "wide_gqa_decode": dict(
+        kind="decode", B=256, lens=("uniform", 128, 2048), block_size=256,
+        H_q=64, H_kv=8, d=128, layers=1,
+    ),
 }
 
-CONFIG_ORDER = ["tiny_decode", "qwen3_decode", "long_decode", "prefix_prefill", "full_step"]
+CONFIG_ORDER = ["tiny_decode", "qwen3_decode", "long_decode", "prefix_prefill", "full_step",
+                "wide_gqa_decode"]
 
 
 def config_seed(name: str) -> int:
