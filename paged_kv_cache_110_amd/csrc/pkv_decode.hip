@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   constexpr int kQBufs = NBUF > 2 ? 2 : 1;
   // VALU form: lane-group layout, q[g] words of this lane's d chunk.  MFMA
   // form (QM): the B operand of the score MFMA, column mcol = head mcol of
-  // the group (zero past G), d = 32 * ks + 8 * mq .. + 7 for k-step ks.
+  // the group (zero past G), d chunk KSM * mq + ks (8 elements) for k-step ks.
   constexpr int KSM = D / 32;  // k-steps of the score MFMA
   constexpr int DBM = D / 16;  // 16-row d blocks of O^T
   const int mcol = lane & 15;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     if constexpr (MF) {
 #pragma unroll
       for (int ks = 0; ks < KSM; ++ks)
-        dst.k[ks] = mcol < G ? ld16(q + (head0 + mcol) * D + 32 * ks + 8 * mq) : u32x4{0, 0, 0, 0};
+        dst.k[ks] = mcol < G ? ld16(q + (head0 + mcol) * D + 8 * (KSM * mq + ks)) : u32x4{0, 0, 0, 0};
     } else {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -463,9 +463,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   };
 
   // MFMA form: element offset of 16-byte chunk c of row r (0..15) of a staged
-  // K or V tile.  The XOR keeps the chunk stores (16 lanes per row), the K
-  // operand reads (16 rows, one chunk) and the transposing V reads (8 rows x
-  // 2 chunks per 32 lanes) free of LDS bank conflicts.
+  // K or V tile, chunks XOR-swizzled by row.  With this swizzle the chunk
+  // stores (16 lanes per row), the transposing V reads and the K operand reads
+  // (quarter mq of k-step ks reads chunk KSM * mq + ks of row mcol) measure
+  // free of LDS bank conflicts (SQ_LDS_BANK_CONFLICT).  The order of the d
+  // chunks over the k-steps is free, since q is laid out the same way; the
+  // order 4 * ks + mq conflicted (about 4 stall cycles per K read).
   auto mf_off = [&](int r, int c) {
     const int sw = D == 128 ? 2 * (r & 7) + (r >> 3) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
     return r * D + ((c ^ sw) << 3);
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSM; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + mf_off(mcol, 4 * ks + mq));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + mf_off(mcol, KSM * mq + ks));
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                      __builtin_bit_cast(bf16x8, qw.k[ks]), st, 0, 0, 0);
       }
