@@ -10,7 +10,7 @@ import torch
 import oracle as O
 import paged_kv_cache_110_amd as pkv
 from paged_kv_cache_110_amd import _lib
-from workloads import SeqState, custom_plan, make_plan
+from workloads import SeqState, custom_plan, make_plan, CONFIG_ORDER
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pkv.h")
@@ -142,8 +142,7 @@ def _meta_equal(a, b):
     assert a["block_tables"].tolist() == b["block_tables"]
 
 
-@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_decode", "long_decode", "prefix_prefill",
-                                  "full_step"])
+@pytest.mark.parametrize("name", CONFIG_ORDER)
 def test_prepare_metadata_matches_oracle(name):
     plan = make_plan(name)
     got = pkv.prepare_metadata(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
