@@ -56,9 +56,14 @@ def store_bytes(plan) -> int:
     return 2 * n * plan.row_elems * 2 * 2 + 4 * n
 
 
+def causal_pairs(num_cached: int, num_new: int) -> int:
+    """Unmasked (query, key) pairs of one sequence: query i sees keys 0 .. c + i."""
+    return num_new * num_cached + num_new * (num_new + 1) // 2
+
+
 def prefill_flops(plan) -> int:
     """Causal attention flops over unmasked (query, key) pairs: 4 d H_q per pair."""
-    pairs = sum(s.num_new * s.num_cached + s.num_new * (s.num_new + 1) // 2 for s in plan.seqs)
+    pairs = sum(causal_pairs(s.num_cached, s.num_new) for s in plan.seqs)
     return 4 * plan.d * plan.H_q * pairs
 
 
@@ -208,7 +213,7 @@ def run_packed(steps, warmup, torch, pkv, log):
     torch.cuda.synchronize()
     ms = events_ms(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out),
                    steps)
-    fl = 4 * cfg["d"] * cfg["H_q"] * sum(n * (n + 1) // 2 for n in lens)
+    fl = 4 * cfg["d"] * cfg["H_q"] * sum(causal_pairs(0, n) for n in lens)
     tf = fl / (ms * 1e-3) / 1e12
     return dict(workload="packed_prefill", B=cfg["B"], tokens=sum(lens), attn_ms=round(ms, 4),
                 prefill_tflops=round(tf, 2), prefill_pct_mfma_peak=round(100 * tf / BF16_PEAK_TFLOPS, 2),
