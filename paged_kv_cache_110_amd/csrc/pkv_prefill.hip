@@ -41,6 +41,8 @@
 //    at about the same time: those hit in the XCD's L2.  (Query tile
 //    outermost spread each XCD over every sequence at once and fetched about
 //    13 times the K/V bytes from HBM.)
+#include <type_traits>
+
 #include "device_common.h"
 #include "pkv_internal.h"
 
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
   const int h_kv = blockIdx.x;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int lane = tid & 63;
   const int H_q = H_kv * G;
 
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx *= scale_log2e;  // the scale is positive: max commutes with it
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    mx = cross_reduce<32, true>(mx);  // with lane l ^ 32, on the VALU (v_permlane32_swap)
     if (__any(mx > m + kPrefillLazy)) {
       const float mn = fmaxf(m, mx);
       const float alpha = fast_exp2(m - mn);
@@ -356,9 +358,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
   load_tile(0);
   stash_tile(lds, lds + TILE);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    uint16_t* cur = lds + (kt & 1) * 2 * TILE;
-    uint16_t* nxt = lds + ((kt + 1) & 1) * 2 * TILE;
+  // Tile kt computes from LDS buffer kt & 1 and stages tile kt + 1 into the
+  // other.  The loop runs two tiles per iteration so that each buffer's base
+  // is a constant: the LDS operand addresses are then loop-invariant
+  // registers plus immediate offsets.
+  auto tile_step = [&](int kt, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    uint16_t* cur = lds + BUF * 2 * TILE;
+    uint16_t* nxt = lds + (1 - BUF) * 2 * TILE;
     const bool more = kt + 1 < ntiles;
     if (more) load_tile(kt + 1);
     // a tile wholly past this wavefront's last position is masked out for all
@@ -372,6 +379,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
     }
     if (more) stash_tile(nxt, nxt + TILE);
     __syncthreads();
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile_step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < ntiles) tile_step(kt + 1, std::integral_constant<int, 1>{});
   }
 
   l += shfl_xor_f32(l, 32);
