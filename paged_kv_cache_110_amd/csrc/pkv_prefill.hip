@@ -170,6 +170,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
   const int64_t row_stride = k_stride;  // elements between K token rows (paged: == v_stride)
   const int64_t goff = r0 * row_stride + ch * 8;  // element offset of this thread's first row
   const int64_t goff_v = r0 * v_stride + ch * 8;
+  // the same in bytes, and the bytes between load passes, for the buffer loads
+  // of whole tiles (a tile spans less than 2^31 bytes from its first row)
+  const int32_t goff_b = (int32_t)(goff * 2);
+  const int32_t goff_vb = (int32_t)(goff_v * 2);
+  const int32_t pass_kb = (int32_t)(RPP * row_stride * 2);
+  const int32_t pass_vb = (int32_t)(RPP * v_stride * 2);
   // the LDS slot of this thread's chunk; rows r0 + RPP * p share their low four bits
   const int soff = r0 * D + ((ch ^ swz<CPR>(r0)) << 3);
   // K operand reads: row kb * 32 + mrow, logical chunk 2 * ks + half.  The row
@@ -205,20 +211,29 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
   // look-ups first).  Rows past the keys this workgroup needs, or behind an
   // out-of-range block id, read valid memory and are zeroed when stashed.
   const bool tile_in_block = bs_log2 >= 6;
+  // Whole tile from its first K and V rows: buffer loads whose base (a
+  // scalar resource) moves per tile while the lane and pass offsets stay
+  // fixed, so no 64-bit address is computed per load.
+  auto load_rows = [&](const uint16_t* kb, const uint16_t* vb) {
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kb), (short)0,
+                                                      0x7FFFFFFF, 0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vb), (short)0,
+                                                      0x7FFFFFFF, 0x00020000);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      kr[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, goff_b, p * pass_kb, 0);
+      vr[p] = __builtin_amdgcn_raw_buffer_load_b128(rv, goff_vb, p * pass_vb, 0);
+    }
+  };
   auto load_tile = [&](int kt) {
     if constexpr (!PAGED) {
       // consecutive token rows; rows past kend re-read the last key (zeroed when stashed)
       // (rows are also kept inside [0, total_k) whatever cu_k holds)
       const int j0 = kt * BN;
       if (j0 + BN <= kend && kb0 >= 0 && (int64_t)kb0 + j0 + BN <= num_blocks) {
-        const uint16_t* kb = khead + ((int64_t)kb0 + j0) * k_stride;
-        const uint16_t* vb = vhead + ((int64_t)kb0 + j0) * v_stride;
+        load_rows(khead + ((int64_t)kb0 + j0) * k_stride, vhead + ((int64_t)kb0 + j0) * v_stride);
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-          kok[p] = true;
-          kr[p] = ld16(kb + (int64_t)RPP * p * k_stride + goff);
-          vr[p] = ld16(vb + (int64_t)RPP * p * v_stride + goff_v);
-        }
+        for (int p = 0; p < PASSES; ++p) kok[p] = true;
         full_next = true;
       } else {
 #pragma unroll
@@ -239,14 +254,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
       const bool blk_ok = (unsigned)blk < (unsigned)num_blocks;
       blk = blk_ok ? blk : 0;
       const int64_t base = (((int64_t)blk << bs_log2) + ((kt * BN) & bmask)) * row_stride;
-      const uint16_t* kb = khead + base;
-      const uint16_t* vb = vhead + base;
+      load_rows(khead + base, vhead + base);
 #pragma unroll
-      for (int p = 0; p < PASSES; ++p) {
-        kok[p] = blk_ok && kt * BN + r0 + RPP * p < kend;
-        kr[p] = ld16(kb + (int64_t)RPP * p * row_stride + goff);
-        vr[p] = ld16(vb + (int64_t)RPP * p * row_stride + goff_v);
-      }
+      for (int p = 0; p < PASSES; ++p) kok[p] = blk_ok && kt * BN + r0 + RPP * p < kend;
       full_next = blk_ok && kt * BN + BN <= kend;
     } else {
       int blk[PASSES];
