@@ -349,12 +349,14 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
         }
   };
   auto pv_mfma = [&](const uint16_t* vt_lds, const f16x8 (&pf)[2][2]) {
+    // key slice outermost: the four d blocks' MFMAs of one slice are
+    // independent, and each slice needs only its own 8 exponentials
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int db = 0; db < DB; ++db) {
           const int rofs = (kb * 32 + 16 * s2) * D;
           const i16x4 va = lds_read_tr16(vt_lds + (voff[0] ^ (32 * db)) + rofs);
           const i16x4 vb = lds_read_tr16(vt_lds + (voff[1] ^ (32 * db)) + rofs);
