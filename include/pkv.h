@@ -187,8 +187,9 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
  * magnitude are rounded to fp16 subnormals (absolute error below 2^-25).
  * PKV_EINVAL / PKV_EUNSUPPORTED as for pkv_decode, plus total_q < 0,
  * max_seqlen_q < 0 or B > 65535 (PKV_EINVAL), and max_seqlen_q above
- * 65535 query tiles of 128 / G positions (PKV_EUNSUPPORTED).  B == 0,
- * total_q == 0 or max_seqlen_q == 0 enqueues nothing.
+ * 65535 query tiles of 128 / G positions or H_kv * d above 2^24
+ * (PKV_EUNSUPPORTED).  B == 0, total_q == 0 or max_seqlen_q == 0 enqueues
+ * nothing.
  */
 pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_tables,
@@ -222,8 +223,9 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
  * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, a stride
  * below the row size or not a multiple of 8, misaligned pointers, B < 0,
  * B > 65535, total_q < 0, total_k < 0, or total_k == 0 with work to do.
- * PKV_EUNSUPPORTED: d not in {64, 128}, H_q/H_kv not in {1, 2, 4, 8}, or
- * max_seqlen_q above 65535 query tiles of 128 / G positions.
+ * PKV_EUNSUPPORTED: d not in {64, 128}, H_q/H_kv not in {1, 2, 4, 8},
+ * max_seqlen_q above 65535 query tiles of 128 / G positions, or k_stride or
+ * v_stride above 2^24 elements.
  * B == 0, total_q == 0 or max_seqlen_q == 0 enqueues nothing.
  */
 pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride, const void* k,

@@ -189,6 +189,7 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
   if (B > 65535) return PKV_EINVAL;
   if (pkv::prefill_query_tiles(max_seqlen_q, H_q / H_kv) > pkv::kPrefillMaxQueryTiles)
     return PKV_EUNSUPPORTED;
+  if ((int64_t)H_kv * d > pkv::kPrefillMaxRowStride) return PKV_EUNSUPPORTED;
   return launch_status(pkv::launch_prefill(
       static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_tables,
@@ -215,6 +216,8 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
   if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return PKV_EINVAL;
   if (!supported_d(d) || !supported_group(H_q, H_kv)) return PKV_EUNSUPPORTED;
   if (pkv::prefill_query_tiles(max_seqlen_q, H_q / H_kv) > pkv::kPrefillMaxQueryTiles)
+    return PKV_EUNSUPPORTED;
+  if (k_stride > pkv::kPrefillMaxRowStride || v_stride > pkv::kPrefillMaxRowStride)
     return PKV_EUNSUPPORTED;
   return launch_status(pkv::launch_prefill_packed(
       static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q), q_stride,

@@ -59,6 +59,9 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
 // Query tiles of a prefill call (the grid's y extent, at most 65535).
 int64_t prefill_query_tiles(int32_t max_seqlen_q, int32_t G);
 constexpr int64_t kPrefillMaxQueryTiles = 65535;
+// K/V rows of one 64-key tile are addressed with 32-bit byte offsets from the
+// tile's first row, so a row stride (elements) may be at most 2^24.
+constexpr int64_t kPrefillMaxRowStride = (int64_t)1 << 24;
 
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                           const uint16_t* v_cache, const int32_t* block_tables,

@@ -90,6 +90,8 @@ def test_attention_argument_checks_before_launch():
 
     assert pf(H_q=6, H_kv=4) == 1
     assert pf(d=256) == 2
+    hk = (1 << 17) + 1                    # H_kv * d just above 2^24 elements per row
+    assert pf(H_q=hk, H_kv=hk, d=128) == 2
     # more query tiles (of 128 / G positions) than the grid's 65535
     too_many = 65535 * 64 + 1
     assert lib.pkv_prefill_varlen(p, p, p, p, p, p, p, 2, 10, too_many, 10, 4, 2, 64, 8, 16, 3,
@@ -118,6 +120,8 @@ def test_packed_prefill_argument_checks_before_launch():
     assert pk(d=96, qs=768, ks=384, vs=384) == 2
     assert pk(H_q=64, H_kv=4, qs=4096) == 2  # group of 16
     assert pk(mq=65535 * 128 // 2 + 1) == 2  # more than 65535 query tiles (G = 2)
+    big = (1 << 24) + 8
+    assert pk(ks=big) == 2 and pk(vs=big) == 2   # row strides past the 32-bit tile offsets
 
 
 def test_workspace_size_formula():
