@@ -8,8 +8,10 @@
 // that more wavefronts start at once (small batches are latency-bound) while
 // segments are not cut into more pieces than the merge gathers quickly.
 // Larger calls:
-// Level 0: one static share of S0 units per wavefront, about 40% of the
-// work, ending at unit P1.  Levels 1..kLevels-2 hold N = ceil(W / 2) shares
+// Level 0: one static share of S0 units per wavefront, ending at unit P1:
+// about 60% of the work for calls of at most kMidStaticUnits units per
+// wavefront, 40% for larger ones (a small call loses more to share changes
+// and split pieces, a large one more to wavefronts drifting apart).  Levels 1..kLevels-2 hold N = ceil(W / 2) shares
 // each and are handed out in order through an atomic counter: level 1's
 // shares hold S1 units (what is left, spread over 2W), each further level
 // three quarters as many (at least kDynMinUnits).  The last level has W
@@ -33,8 +35,12 @@ namespace pkv {
 
 struct ShareSchedule {
 #ifndef PKV_SCHED_STATIC_NUM
-#define PKV_SCHED_STATIC_NUM 2  // static part: 2/5 of the work
+#define PKV_SCHED_STATIC_NUM 2  // static part of large calls: 2/5 of the work
 #define PKV_SCHED_STATIC_DEN 5
+#endif
+#ifndef PKV_SCHED_MID_STATIC_NUM
+#define PKV_SCHED_MID_STATIC_NUM 3  // static part of calls up to kMidStaticUnits per wavefront: 3/5
+#define PKV_SCHED_MID_STATIC_DEN 5
 #endif
 #ifndef PKV_SCHED_DYN_MIN
 #define PKV_SCHED_DYN_MIN 16
@@ -47,6 +53,7 @@ struct ShareSchedule {
 #endif
   static constexpr int kLevels = 16;
   static constexpr int kMinStaticUnits = 8;
+  static constexpr int kMidStaticUnits = 128;
   static constexpr int kDynMinUnits = PKV_SCHED_DYN_MIN;
 
   int T, W, S0, P1, S1, N;
@@ -60,7 +67,10 @@ struct ShareSchedule {
     if (per_wave <= kMinStaticUnits) {
       s.S0 = per_wave < PKV_SCHED_SMALL_MIN ? PKV_SCHED_SMALL_MIN : (int)per_wave;
     } else {
-      const int s0 = (int)(((int64_t)T * PKV_SCHED_STATIC_NUM / PKV_SCHED_STATIC_DEN) / W);
+      const bool mid = per_wave <= kMidStaticUnits;
+      const int64_t num = mid ? PKV_SCHED_MID_STATIC_NUM : PKV_SCHED_STATIC_NUM;
+      const int64_t den = mid ? PKV_SCHED_MID_STATIC_DEN : PKV_SCHED_STATIC_DEN;
+      const int s0 = (int)(((int64_t)T * num / den) / W);
       s.S0 = s0 < kMinStaticUnits ? kMinStaticUnits : s0;
     }
     s.P1 = (int64_t)s.S0 * W < T ? s.S0 * W : T;
