@@ -3,7 +3,7 @@
 // for W wavefronts.  Plain C++ usable on the host and the device, so the
 // layout can be checked on the CPU.
 //
-// A call of at most kMinStaticUnits units per wavefront is one static pass
+// A call of at most kOnePassUnits units per wavefront is one static pass
 // of ceil(T / W) units per wavefront, but at least PKV_SCHED_SMALL_MIN, so
 // that more wavefronts start at once (small batches are latency-bound) while
 // segments are not cut into more pieces than the merge gathers quickly.
@@ -53,6 +53,9 @@ struct ShareSchedule {
 #endif
   static constexpr int kLevels = 16;
   static constexpr int kMinStaticUnits = 8;
+  // Up to this many units per wavefront, one even static pass beats dynamic
+  // shares, whose 16-unit minimum would leave most wavefronts idle.
+  static constexpr int kOnePassUnits = 32;
   static constexpr int kMidStaticUnits = 128;
   static constexpr int kDynMinUnits = PKV_SCHED_DYN_MIN;
 
@@ -64,7 +67,7 @@ struct ShareSchedule {
     s.T = T;
     s.W = W;
     const int64_t per_wave = ((int64_t)T + W - 1) / W;
-    if (per_wave <= kMinStaticUnits) {
+    if (per_wave <= kOnePassUnits) {
       s.S0 = per_wave < PKV_SCHED_SMALL_MIN ? PKV_SCHED_SMALL_MIN : (int)per_wave;
     } else {
       const bool mid = per_wave <= kMidStaticUnits;

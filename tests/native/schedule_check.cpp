@@ -9,7 +9,7 @@
 //   5. no more than max_shares(W) shares; dynamic shares shrink (never grow)
 //      from one level to the next, except for the last level (W shares that
 //      split whatever remains);
-//   6. a call of at most kMinStaticUnits units per wavefront is static and
+//   6. a call of at most kOnePassUnits units per wavefront is static and
 //      gives no wavefront more than max(ceil(T / W), PKV_SCHED_SMALL_MIN) units.
 #include <cstdio>
 #include <cstdint>
@@ -60,7 +60,7 @@ static int check(int T, int W) {
   }
   if (next != T) return fail("coverage", T, W, next, 0);
   const long long per_wave = ((long long)T + W - 1) / W;
-  if (per_wave <= pkv::ShareSchedule::kMinStaticUnits) {
+  if (per_wave <= pkv::ShareSchedule::kOnePassUnits) {
     if (s.dynamic()) return fail("small call not static", T, W, per_wave, 0);
     for (int k = 0; k < W; ++k) {
       int st = 0, en = 0;
