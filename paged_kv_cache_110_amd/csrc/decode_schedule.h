@@ -55,7 +55,7 @@ struct ShareSchedule {
   static constexpr int kMinStaticUnits = 8;
   // Up to this many units per wavefront, one even static pass beats dynamic
   // shares, whose 16-unit minimum would leave most wavefronts idle.
-  static constexpr int kOnePassUnits = 32;
+  static constexpr int kOnePassUnits = 64;
   static constexpr int kMidStaticUnits = 128;
   static constexpr int kDynMinUnits = PKV_SCHED_DYN_MIN;
 

@@ -1,5 +1,5 @@
 """Decode parity on batches large enough that the kernel's work schedule hands
-out dynamic shares (more than 32 16-token tiles per resident wavefront):
+out dynamic shares (more than 64 16-token tiles per resident wavefront):
 long segments cut into many pieces, batches beyond the sequences whose
 offsets the kernel keeps in LDS, padding rows, and a workspace reused across
 calls.  Every output is compared with the float64 oracle."""
@@ -59,7 +59,7 @@ def test_decode_dynamic_schedule(geom):
     g = torch.Generator().manual_seed(11 + sum(geom))
     # enough tiles that the schedule goes dynamic for every head count: a few
     # very long sequences (many pieces each), many mid-size ones, some short
-    units_wanted = 100_000
+    units_wanted = 160_000
     lens = [30_000, 17, 1, 9_000]
     while sum(-(-n // 16) for n in lens) * H_kv < units_wanted:
         lens.append(int(torch.randint(1, 6_000, (1,), generator=g)))
