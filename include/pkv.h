@@ -155,7 +155,8 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d
  * wavefront took which share: results are deterministic run to run on one
  * device.
  * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, block_size
- * not a power of two >= 16, misaligned pointers, too small a workspace.
+ * not a power of two >= 16, misaligned pointers, too small a workspace, a
+ * softmax_scale that is not finite.
  * PKV_EUNSUPPORTED: d not in {64, 128}; H_q/H_kv not in {1, 2, 4, 8};
  * B * H_kv * ceil(max_blocks_per_seq * block_size / 16) > INT32_MAX.
  */
@@ -186,7 +187,8 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
  * (|v| <= 65504; larger values give non-finite rows); V values under 2^-14 in
  * magnitude are rounded to fp16 subnormals (absolute error below 2^-25).
  * PKV_EINVAL / PKV_EUNSUPPORTED as for pkv_decode, plus total_q < 0,
- * max_seqlen_q < 0 or B > 65535 (PKV_EINVAL), and max_seqlen_q above
+ * max_seqlen_q < 0, B > 65535 or a softmax_scale that is not finite and
+ * positive (PKV_EINVAL), and max_seqlen_q above
  * 65535 query tiles of 128 / G positions or H_kv * d above 2^24
  * (PKV_EUNSUPPORTED).  B == 0, total_q == 0 or max_seqlen_q == 0 enqueues
  * nothing.
@@ -222,7 +224,8 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
  * Precision as for pkv_prefill_varlen (V within fp16's range).
  * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, a stride
  * below the row size or not a multiple of 8, misaligned pointers, B < 0,
- * B > 65535, total_q < 0, total_k < 0, or total_k == 0 with work to do.
+ * B > 65535, total_q < 0, total_k < 0, total_k == 0 with work to do, or a
+ * softmax_scale that is not finite and positive.
  * PKV_EUNSUPPORTED: d not in {64, 128}, H_q/H_kv not in {1, 2, 4, 8},
  * max_seqlen_q above 65535 query tiles of 128 / G positions, or k_stride or
  * v_stride above 2^24 elements.

@@ -3,6 +3,7 @@
 #include "pkv.h"
 
 #include <limits.h>
+#include <math.h>
 
 #include <algorithm>
 #include <vector>
@@ -28,6 +29,11 @@ bool decode_units_fit(int32_t B, int32_t H_kv, int32_t block_size, int32_t max_b
   const int64_t tiles = ((int64_t)max_blocks_per_seq * block_size + 15) / 16;
   return (int64_t)B * H_kv * tiles <= INT32_MAX;
 }
+
+// The prefill kernels take the running maximum of the raw scores and scale
+// it afterwards, which is only the maximum of the scaled scores for a
+// positive scale.
+bool positive_finite(float x) { return isfinite(x) && x > 0.0f; }
 
 pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
 
@@ -154,7 +160,7 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
                       int32_t H_q, int32_t H_kv, int32_t d, int32_t num_blocks,
                       int32_t block_size, int32_t max_blocks_per_seq, float softmax_scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (B <= 0 || !context_lens) return PKV_EINVAL;
+  if (B <= 0 || !context_lens || !isfinite(softmax_scale)) return PKV_EINVAL;
   pkv_status st = check_attention(out, q, k_cache, v_cache, block_tables, H_q, H_kv, d,
                                   num_blocks, block_size, max_blocks_per_seq);
   if (st != PKV_OK) return st;
@@ -182,7 +188,7 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
   (void)max_seqlen_k;
   if (B < 0 || total_q < 0 || max_seqlen_q < 0) return PKV_EINVAL;
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return PKV_OK;
-  if (!cu_seqlens_q || !cu_seqlens_k) return PKV_EINVAL;
+  if (!cu_seqlens_q || !cu_seqlens_k || !positive_finite(softmax_scale)) return PKV_EINVAL;
   pkv_status st = check_attention(out, q, k_cache, v_cache, block_tables, H_q, H_kv, d,
                                   num_blocks, block_size, max_blocks_per_seq);
   if (st != PKV_OK) return st;
@@ -208,6 +214,7 @@ pkv_status pkv_prefill_varlen_packed(void* out, const void* q, int64_t q_stride,
   if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0) return PKV_EINVAL;
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return PKV_OK;
   if (!out || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_k) return PKV_EINVAL;
+  if (!positive_finite(softmax_scale)) return PKV_EINVAL;
   if (H_q <= 0 || H_kv <= 0 || d <= 0 || H_q % H_kv != 0 || total_k <= 0) return PKV_EINVAL;
   if (B > 65535) return PKV_EINVAL;
   const int64_t qrow = (int64_t)H_q * d, kvrow = (int64_t)H_kv * d;

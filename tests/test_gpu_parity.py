@@ -1,10 +1,11 @@
 """HIP path (through the C ABI) against the CPU oracle, on the GPU.
 
-Bars: the store and the cache contents bit-exact; attention outputs within
-max-abs 1e-2 of the float64 oracle (bf16 inputs, fp32 accumulation, bf16
-output).  Small cases compare every output; the full-size workloads compare
-sampled outputs that the oracle computes one by one, in the same launch
-configuration the benchmark times.
+Bars: the store and the cache contents bit-exact; each attention output
+within 1e-2 of the float64 oracle or equal to one of the two bf16 values that
+bracket the oracle's value (``gpu_harness.within_bar``).  Small cases and the
+decode workloads at full size compare every output; the full-size prefill
+workloads compare every row of the shared-prefix sequences plus sampled rows
+of the rest, in the same launch configuration the benchmark times.
 """
 import math
 
@@ -164,25 +165,10 @@ def test_permutation_invariance_and_determinism(kind):
 # ------------------------------------------------------------ full sizes
 
 
-def _sample(n, k, seed):
-    g = torch.Generator().manual_seed(seed)
-    idx = torch.randperm(n, generator=g)[:k].tolist()
-    return sorted(idx)
-
-
-def _check_decode_sample(plan, host, meta_full, out, layer, idx, what):
-    sub = plan.subset(idx)
-    om = O.prepare_decode(sub.seqs, plan.block_size, plan.max_blocks_per_seq)
-    q = host.q[layer][idx]
-    ref = O.default().decode(q, host.k_cache(0 if host.pool.shape[1] == 1 else layer),
-                             host.v_cache(0 if host.pool.shape[1] == 1 else layer),
-                             om["block_tables"], om["context_lens"], scale_of(plan.d))
-    assert_close(out[idx], ref, what)
-
-
-@pytest.mark.parametrize("name,nsample", [("qwen3_decode", 48), ("long_decode", 6),
-                                          ("wide_gqa_decode", 24)])
-def test_full_size_decode(name, nsample):
+@pytest.mark.parametrize("name", ["qwen3_decode", "long_decode", "wide_gqa_decode"])
+def test_full_size_decode(name):
+    """The whole workload, every output compared: the oracle's decode of all
+    sequences takes well under a second on the host cores."""
     log(f"full-size {name}")
     plan = make_plan(name)
     tens = make_tensors(plan, DEV, poison=True)
@@ -193,15 +179,12 @@ def test_full_size_decode(name, nsample):
     out = gpu_attention(plan, tens, dm)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    oracle_store(host, oracle_meta(plan))
+    ometa = oracle_meta(plan)
+    oracle_store(host, ometa)
     assert_bits_equal(tens.k_cache(), host.k_cache(), f"{name} k_cache after store")
     assert_bits_equal(tens.v_cache(), host.v_cache(), f"{name} v_cache after store")
-    # longest and shortest sequences always sampled (most splits / one split)
-    lens = plan.lens()
-    idx = set(_sample(plan.B, nsample, 11))
-    idx.add(max(range(plan.B), key=lambda b: lens[b]))
-    idx.add(min(range(plan.B), key=lambda b: lens[b]))
-    _check_decode_sample(plan, host, meta, out, 0, sorted(idx), f"{name} sampled sequences")
+    ref = oracle_attention(plan, host, ometa)
+    assert_close(out, ref, f"{name} all {plan.B} sequences")
 
 
 def test_full_size_prefix_prefill():
@@ -234,8 +217,13 @@ def test_full_size_prefix_prefill():
     ref = O.default().decode(host.q[0][rows], host.k_cache(), host.v_cache(), tables, ctx,
                              scale_of(plan.d))
     assert_close(out[rows], ref, "prefix_prefill sampled rows")
-    # sequences 0..3 share their first 8 blocks
-    assert plan.seqs[0].block_ids[:8] == plan.seqs[3].block_ids[:8]
+    # sequences 0..3 share their first 8 blocks: every row of the four, by the
+    # oracle's own prefill over those sequences
+    assert all(plan.seqs[b].block_ids[:8] == plan.seqs[0].block_ids[:8] for b in range(4))
+    cq, ck = ometa["cu_seqlens_q"][:5], ometa["cu_seqlens_k"][:5]
+    ref4 = O.default().prefill(host.q[0][: cq[4]], host.k_cache(), host.v_cache(),
+                               ometa["block_tables"][:4], cq, ck, scale_of(plan.d))
+    assert_close(out[: cq[4]], ref4, f"prefix_prefill all {cq[4]} rows of the shared-prefix sequences")
 
 
 def test_full_size_full_step():
@@ -253,21 +241,16 @@ def test_full_size_full_step():
         outs.append(gpu_attention(plan, tens, dm, layer))
     torch.cuda.synchronize()
     ometa = oracle_meta(plan)
-    idx = _sample(plan.B, 24, 12)
-    lens = plan.lens()
-    idx = sorted(set(idx) | {max(range(plan.B), key=lambda b: lens[b])})
     for j, layer in enumerate(check_layers):
         log(f"full_step layer {layer}")
         O.default().store(host.k_cache(j), host.v_cache(j), host.k_new(layer), host.v_new(layer),
                           ometa["slot_mapping"])
         assert_bits_equal(tens.k_cache(layer), host.k_cache(j), f"layer {layer} k_cache")
         assert_bits_equal(tens.v_cache(layer), host.v_cache(j), f"layer {layer} v_cache")
-        sub = plan.subset(idx)
-        om = O.prepare_decode(sub.seqs, plan.block_size, plan.max_blocks_per_seq)
-        ref = O.default().decode(host.q[layer][idx], host.k_cache(j), host.v_cache(j),
-                                 om["block_tables"], om["context_lens"], scale_of(plan.d))
+        ref = O.default().decode(host.q[layer], host.k_cache(j), host.v_cache(j),
+                                 ometa["block_tables"], ometa["context_lens"], scale_of(plan.d))
         assert torch.isfinite(outs[layer].float()).all()
-        assert_close(outs[layer][idx], ref, f"full_step layer {layer} sampled sequences")
+        assert_close(outs[layer], ref, f"full_step layer {layer}, all {plan.B} sequences")
     del tens
     torch.cuda.empty_cache()
 

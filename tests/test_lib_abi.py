@@ -90,6 +90,12 @@ def test_attention_argument_checks_before_launch():
 
     assert pf(H_q=6, H_kv=4) == 1
     assert pf(d=256) == 2
+    nan, inf = float("nan"), float("inf")
+    for bad in (0.0, -0.125, nan, inf):   # the prefill scale must be finite and positive
+        assert lib.pkv_prefill_varlen(p, p, p, p, p, p, p, 2, 10, 10, 10, 4, 2, 64, 8, 16, 3,
+                                      bad, None) == 1
+    for bad in (nan, inf, -inf):          # the decode scale must be finite
+        assert lib.pkv_decode(p, p, p, p, p, p, 2, 4, 2, 64, 8, 16, 3, bad, p, 1 << 20, None) == 1
     hk = (1 << 17) + 1                    # H_kv * d just above 2^24 elements per row
     assert pf(H_q=hk, H_kv=hk, d=128) == 2
     # more query tiles (of 128 / G positions) than the grid's 65535
@@ -105,9 +111,10 @@ def test_packed_prefill_argument_checks_before_launch():
     buf = ctypes.create_string_buffer(4096 + 16)
     p = (ctypes.addressof(buf) + 15) // 16 * 16
 
-    def pk(qs=512, ks=256, vs=256, B=2, tq=10, tk=10, mq=10, H_q=8, H_kv=4, d=64, q=p):
+    def pk(qs=512, ks=256, vs=256, B=2, tq=10, tk=10, mq=10, H_q=8, H_kv=4, d=64, q=p,
+           scale=0.125):
         return lib.pkv_prefill_varlen_packed(p, q, qs, p, ks, p, vs, p, p, B, tq, tk, mq, mq,
-                                             H_q, H_kv, d, 0.125, None)
+                                             H_q, H_kv, d, scale, None)
 
     assert pk(B=0) == 0 and pk(tq=0) == 0 and pk(mq=0) == 0   # nothing to do
     assert pk(qs=256) == 1        # q stride below H_q * d
@@ -117,6 +124,8 @@ def test_packed_prefill_argument_checks_before_launch():
     assert pk(q=p + 2) == 1       # misaligned
     assert pk(tk=0) == 1          # no keys
     assert pk(B=-1) == 1
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert pk(scale=bad) == 1
     assert pk(d=96, qs=768, ks=384, vs=384) == 2
     assert pk(H_q=64, H_kv=4, qs=4096) == 2  # group of 16
     assert pk(mq=65535 * 128 // 2 + 1) == 2  # more than 65535 query tiles (G = 2)
