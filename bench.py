@@ -4,22 +4,27 @@
 A step is one pass of the whole path over one batch of seeded synthetic input:
 the host metadata is prepared once (outside the timed region), then each step
 stores the new K/V rows (pkv_store) and runs attention (pkv_decode, or
-pkv_prefill_varlen for the prefill workload); the 28-layer workload does both
-for every layer.  Inputs are resident in HBM before timing starts.
+pkv_prefill_varlen for the prefill workload), for every layer of the workload.
+Inputs are resident in HBM before timing starts.
 
-The JSON line reports the Qwen3-0.6B-shaped decode workload (B=256, H_q=16,
-H_kv=8, d=128, block size 256, context lengths U[128, 2048]) with its decode
-roofline (achieved algorithmic HBM bytes per decode call / the call's average
-duration) and the CPU oracle timed on a bounded sample.  The other workloads
-are reported under "secondary".
+The JSON line reports the 28-layer decode step (B=512, H_q=32, H_kv=8, d=128,
+block size 256, context lengths log-uniform in [16, 16384], per-layer views of
+one [2, 28, blocks, 256, 8, 128] pool): `value` is the step's algorithmic HBM
+bytes over its wall time; `roofline` is the per-layer pkv_decode call
+(decode_kernel + decode_merge_kernel) against the published HBM peak and
+against a measured ceiling (a load-only probe kernel that reads the same pages
+in the same pattern); `cpu_baseline` is the float64 oracle on the host cores,
+on a bounded sample of the same workload, with its max-abs error against the
+GPU outputs.  The single-layer decode workloads, the prefill workloads and the
+other steps are reported under "secondary", each decode and prefill workload
+with its own roofline, call-time spread and oracle timing.
 
-Timing: the timed region (K steps) holds no events, only the library calls,
-bracketed by synchronisations and the wall clock.  Per-call durations come
-from the same calls run back to back right after it, with one pair of HIP
-events on the launch stream around each run (events recorded between calls
-add their own gaps to what they measure).
+Timing: the timed region (K steps) brackets every attention call with a pair
+of HIP events on the launch stream (torch's current stream, which the library
+uses); median, min and max over those calls are reported, and the wall clock
+around the whole region gives ms_per_step.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -37,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attn: achieved HBM GB/s & % peak; prefill TFLOP/s; tokens/s"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PARITY_TOL = 1e-2           # max-abs bar for bf16 attention outputs
 
 
 # ------------------------------------------------------------ workload arithmetic
@@ -48,6 +55,11 @@ def decode_bytes(plan) -> int:
     qo = 2 * plan.B * plan.H_q * plan.d * 2
     tbl = 4 * sum(-(-n // plan.block_size) for n in plan.lens())
     return kv + qo + 4 * plan.B + tbl
+
+
+def kv_bytes(plan) -> int:
+    """K+V bytes of every context token: what the load-only probe reads."""
+    return sum(2 * n * plan.H_kv * plan.d * 2 for n in plan.lens())
 
 
 def store_bytes(plan) -> int:
@@ -88,20 +100,200 @@ def measured_traffic(workload: str):
 
 # ------------------------------------------------------------------- timing
 
-def events_ms(torch, fn, n):
-    """Average duration of n back-to-back calls fn(i), from one pair of HIP events on
-    the current stream (the stream the library launches on)."""
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(n):
+def spread(ms_list) -> dict:
+    """Median, min, max and mean of per-call durations (ms)."""
+    return dict(median=round(statistics.median(ms_list), 5), min=round(min(ms_list), 5),
+                max=round(max(ms_list), 5), mean=round(statistics.fmean(ms_list), 5),
+                n=len(ms_list))
+
+
+def timed_calls(torch, fn, n):
+    """n calls fn(i), each between its own pair of HIP events on the current
+    stream; returns the per-call durations (ms)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
         fn(i)
-    b.record()
+        b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / n
+    return [a.elapsed_time(b) for a, b in ev]
 
 
-def run_workload(name, steps, warmup, pools, torch, pkv, log):
+# ----------------------------------------------------------------- ceilings
+
+def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dict:
+    """What the device sustains with hand-written probe kernels: a plain
+    streaming read and a plain copy of a buffer of known size, and the dense
+    MFMA issue rate (bf16 and fp16 32x32x16, register operands) at the best of
+    a few occupancies."""
+    n = int(gib * (1 << 30))
+    src = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {}
+    for _ in range(2):
+        probe.read(src, sink)
+        probe.copy(dst, src)
+    rd = timed_calls(torch, lambda i: probe.read(src, sink), runs)
+    cp = timed_calls(torch, lambda i: probe.copy(dst, src), runs)
+    res["read"] = dict(kernel="read_kernel (libpkv_probe)", bytes=n, ms=spread(rd),
+                       gb_per_s=round(n / statistics.median(rd) / 1e6, 1))
+    res["copy"] = dict(kernel="copy_kernel (libpkv_probe)", bytes=2 * n, ms=spread(cp),
+                       gb_per_s=round(2 * n / statistics.median(cp) / 1e6, 1))
+    del src, dst
+    torch.cuda.empty_cache()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    msink = torch.zeros(cus * 4 * 8, dtype=torch.float32, device="cuda")
+    for name, f16 in (("mfma_bf16", False), ("mfma_f16", True)):
+        best = None
+        for waves, chains in ((1, 4), (2, 4), (2, 8), (4, 4)):
+            iters = 2000
+            probe.mfma(msink, cus, waves, iters, chains, f16)
+            ms = timed_calls(torch, lambda i: probe.mfma(msink, cus, waves, iters, chains, f16), 5)
+            flops = cus * 4 * waves * iters * chains * 32768
+            tf = flops / (statistics.median(ms) * 1e-3) / 1e12
+            if best is None or tf > best["tflops"]:
+                best = dict(kernel=f"mfma_kernel ({'f16' if f16 else 'bf16'} 32x32x16, libpkv_probe)",
+                            tflops=round(tf, 1), waves_per_simd=waves, chains=chains,
+                            flops=flops, ms=spread(ms))
+        res[name] = best
+    log(f"ceilings: read {res['read']['gb_per_s']} GB/s, copy {res['copy']['gb_per_s']} GB/s, "
+        f"bf16 MFMA {res['mfma_bf16']['tflops']} TFLOP/s, f16 MFMA {res['mfma_f16']['tflops']} TFLOP/s")
+    return res
+
+
+def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20) -> dict:
+    """The load-only probe over the same pages as the decode (same tables and
+    lengths), rotating over the given (k_cache, v_cache) views so consecutive
+    runs do not find their bytes in the last-level cache."""
+    from paged_kv_cache_110_amd.probe import pages_of
+
+    pages = pages_of(meta["block_tables"], meta["context_lens"], plan.block_size).to("cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def run(i):
+        kc, vc = views[i % len(views)]
+        probe.paged_read(kc, vc, pages, sink)
+
+    for i in range(2):
+        run(i)
+    ms = timed_calls(torch, run, runs)
+    nbytes = kv_bytes(plan)
+    return dict(kernel="paged_read_kernel (libpkv_probe)", bytes=nbytes, ms=spread(ms),
+                gb_per_s=round(nbytes / statistics.median(ms) / 1e6, 1),
+                pages=int(pages.shape[0]))
+
+
+# ------------------------------------------------------------ the oracle leg
+
+def _errors(got, ref, tol=PARITY_TOL):
+    err = (got.double() - ref).abs()
+    return (err.max().item() if err.numel() else 0.0), int((err > tol).sum())
+
+
+def oracle_decode_leg(plan, tens, outs, budget_s, log) -> dict:
+    """The float64 oracle, as it stands, on host copies of the same inputs:
+    store + decode of every sequence, one (pool, layer) unit at a time until
+    about budget_s of oracle compute (each unit at least once for a
+    single-layer workload; layers in order for the multi-layer one).  The
+    device-to-host copy time is counted apart.  Each unit's oracle output is
+    compared with the GPU output of the same unit from the timed steps."""
+    import oracle as O
+
+    orc = O.default()
+    om = O.prepare_decode(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    scale = 1.0 / math.sqrt(plan.d)
+    units = [(r, l) for l in range(plan.layers) for r in range(len(tens))]
+    compute_s = d2h_s = 0.0
+    done, max_err, over, values = 0, 0.0, 0, 0
+    host = {}
+    while done < len(units) or compute_s < budget_s:
+        r, l = units[done % len(units)]
+        if (r, l) not in host:
+            t0 = time.perf_counter()
+            t = tens[r]
+            h = (t.k_cache(l).cpu(), t.v_cache(l).cpu(), t.q[l].cpu(), t.k_new(l).cpu(),
+                 t.v_new(l).cpu(), outs[(r, l)].cpu())
+            d2h_s += time.perf_counter() - t0
+            if plan.layers == 1:
+                host[(r, l)] = h  # small: kept for repeats
+        else:
+            h = host[(r, l)]
+        kc, vc, q, kn, vn, got = h
+        t0 = time.perf_counter()
+        orc.store(kc, vc, kn, vn, om["slot_mapping"])
+        ref = orc.decode(q, kc, vc, om["block_tables"], om["context_lens"], scale)
+        compute_s += time.perf_counter() - t0
+        e, o = _errors(got, ref)
+        max_err, over, values = max(max_err, e), over + o, values + ref.numel()
+        done += 1
+        del h, kc, vc, q, kn, vn, got, ref
+        if plan.layers > 1 and (compute_s >= budget_s or done == len(units)):
+            break
+    per_unit = compute_s / done
+    gbs = (decode_bytes(plan) + store_bytes(plan)) / per_unit / 1e9
+    what = (f"{done} of the {plan.layers} layers" if plan.layers > 1 else
+            f"{done} runs over {len(units)} independent input set(s)")
+    log(f"cpu oracle {plan.name}: {what}, {per_unit * 1e3:.1f} ms per layer step, "
+        f"{orc.threads()} threads, max abs err {max_err:.3e}")
+    return dict(value=round(gbs, 3), unit="GB/s", cores=orc.threads(), kind="oracle",
+                sample=f"{plan.name}: store + decode of all {plan.B} sequences, {what}; float64 C "
+                       f"oracle (OpenMP), {per_unit * 1e3:.1f} ms per layer",
+                ms_per_layer=round(per_unit * 1e3, 2), compute_s=round(compute_s, 2),
+                d2h_s=round(d2h_s, 2), layers_checked=done if plan.layers > 1 else 1,
+                max_abs_err=max_err, values_compared=values, values_over_tol=over,
+                gpu_speedup=None)
+
+
+def oracle_prefill_leg(plan, tens, outs, budget_s, log, tail: int = 64) -> dict:
+    """The oracle's prefill over a stated subset: the last ``tail`` query rows
+    of every sequence, as a prefill chunk behind everything before them (the
+    rows that attend the most keys), repeated up to about budget_s and
+    compared with the GPU's rows for those positions."""
+    import oracle as O
+
+    orc = O.default()
+    om = O.prepare_prefill(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    scale = 1.0 / math.sqrt(plan.d)
+    cu = om["cu_seqlens_q"]
+    rows, cq, ck, pairs = [], [0], [0], 0
+    for b, s in enumerate(plan.seqs):
+        k = min(tail, s.num_new)
+        rows.extend(range(cu[b + 1] - k, cu[b + 1]))
+        cq.append(cq[-1] + k)
+        ck.append(ck[-1] + s.total)
+        pairs += causal_pairs(s.total - k, k)
+    fl = 4 * plan.d * plan.H_q * pairs
+    t0 = time.perf_counter()
+    t = tens[0]
+    kc, vc = t.k_cache().cpu(), t.v_cache().cpu()
+    q = t.q[0].cpu()[rows].contiguous()
+    got = outs[(0, 0)].cpu()[rows]
+    d2h_s = time.perf_counter() - t0
+    reps, compute_s = 0, 0.0
+    while reps == 0 or compute_s < budget_s:
+        t0 = time.perf_counter()
+        ref = orc.prefill(q, kc, vc, om["block_tables"], cq, ck, scale)
+        compute_s += time.perf_counter() - t0
+        reps += 1
+    per = compute_s / reps
+    max_err, over = _errors(got, ref)
+    log(f"cpu oracle {plan.name}: last {tail} rows of each sequence, {per:.2f} s per pass, "
+        f"{orc.threads()} threads, max abs err {max_err:.3e}")
+    return dict(value=round(fl / per / 1e12, 5), unit="TFLOP/s", cores=orc.threads(), kind="oracle",
+                sample=f"{plan.name}: prefill of the last {tail} query rows of each of the {plan.B} "
+                       f"sequences behind their full context ({len(rows)} rows, {fl / 1e9:.1f} "
+                       f"GFLOP), {reps} pass(es); float64 C oracle",
+                s_per_pass=round(per, 3), compute_s=round(compute_s, 2), d2h_s=round(d2h_s, 2),
+                max_abs_err=max_err, values_compared=ref.numel(), values_over_tol=over)
+
+
+# ------------------------------------------------------------ attention workloads
+
+def run_workload(name, steps, warmup, pools, torch, pkv, probe, log, cpu_budget=None):
+    """Timed steps of one named workload, the probe ceiling over the same
+    pages (decode), and the oracle leg (cpu_budget seconds, None = skipped)."""
     from workloads import make_plan, make_tensors
 
     plan = make_plan(name)
@@ -111,15 +303,16 @@ def run_workload(name, steps, warmup, pools, torch, pkv, log):
     meta = pkv.prepare_metadata(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
     dm = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in meta.items()}
     scale = 1.0 / math.sqrt(plan.d)
+    L = plan.layers
     ws = None
     if plan.kind == "decode":
         nbytes = pkv.decode_workspace_size(plan.B, plan.H_q, plan.H_kv, plan.d, plan.block_size,
                                            plan.max_blocks_per_seq)
         ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
-        outs = [torch.empty_like(t.q[0]) for t in tens]
+    outs = {(r, l): torch.empty_like(tens[r].q[l]) for r in range(pools) for l in range(L)}
     torch.cuda.synchronize()
     log(f"{name}: inputs ready in {time.time() - t0:.1f}s ({plan.B} seqs, {plan.num_blocks} blocks,"
-        f" {pools} pool(s))")
+        f" {L} layer(s), {pools} pool(s))")
 
     def store(i, layer):
         t = tens[i % pools]
@@ -129,76 +322,94 @@ def run_workload(name, steps, warmup, pools, torch, pkv, log):
     def attention(i, layer):
         t = tens[i % pools]
         kc, vc = t.k_cache(layer), t.v_cache(layer)
+        out = outs[(i % pools, layer)]
         if plan.kind == "decode":
             pkv.decode(t.q[layer], kc, vc, dm["block_tables"], dm["context_lens"], scale,
-                       out=outs[i % pools], workspace=ws)
+                       out=out, workspace=ws)
         else:
             pkv.prefill_varlen(t.q[layer], kc, vc, dm["block_tables"], dm["cu_seqlens_q"],
-                               dm["cu_seqlens_k"], dm["max_seqlen_q"], dm["max_seqlen_k"], scale)
+                               dm["cu_seqlens_k"], dm["max_seqlen_q"], dm["max_seqlen_k"], scale,
+                               out=out)
 
-    def step(i):
-        for layer in range(plan.layers):
+    for i in range(warmup):
+        for layer in range(L):
             store(i, layer)
             attention(i, layer)
-
-    # the timed region: whole steps, wall clock between synchronisations, no
-    # events inside (recording timing events between calls perturbs them)
-    for i in range(warmup):
-        step(i)
     torch.cuda.synchronize()
+    # the timed region: whole steps; a pair of HIP events around every attention call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps * L)]
     start = time.perf_counter()
     for i in range(steps):
-        step(i)
+        for layer in range(L):
+            store(i, layer)
+            a, b = ev[i * L + layer]
+            a.record()
+            attention(i, layer)
+            b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - start
+    call_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / steps
-
-    # per-call durations: the same calls back to back (pools rotating as in the
-    # steps), one pair of HIP events on the launch stream around each run
-    L = plan.layers
-    attn_ms = events_ms(torch, lambda k: attention(k // L, k % L), steps * L)
-    # store calls back to back are bound by the host's call overhead, not the
-    # GPU: the store's share is the step time per layer minus the attention call
-    store_ms = max(ms_step / L - attn_ms, 0.0)
-    res = dict(plan=plan, ms_per_step=ms_step, attn_ms=attn_ms, store_ms=store_ms)
-    del tens, ws
+    res = dict(plan=plan, ms_per_step=ms_step, call=spread(call_ms))
+    if plan.kind == "decode":
+        views = [(t.k_cache(l), t.v_cache(l)) for l in range(L) for t in tens]
+        res["read_ceiling"] = paged_read_ceiling(torch, probe, plan, meta, views)
+    if cpu_budget is not None:
+        leg = oracle_decode_leg if plan.kind == "decode" else oracle_prefill_leg
+        res["cpu"] = leg(plan, tens, outs, cpu_budget, log)
+    del tens, ws, outs
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(name, budget_s, log):
-    """The oracle (as it stands) on the same workload: one full step (store +
-    attention) repeated until about budget_s of CPU work, inputs on the host."""
-    import torch
+def summarize(res, ceilings) -> dict:
+    """The figures of one attention workload: step throughput, the attention
+    call against its roofline (published peak and measured ceiling), and the
+    oracle leg."""
+    plan = res["plan"]
+    call = res["call"]
+    med_s = call["median"] * 1e-3
+    out = dict(workload=plan.name, layers=plan.layers, ms_per_step=round(res["ms_per_step"], 4),
+               attn_call_ms=call)
+    if plan.kind == "decode":
+        per_call = decode_bytes(plan)
+        per_step = (per_call + store_bytes(plan)) * plan.layers
+        achieved = per_call / med_s / 1e9
+        rc = res["read_ceiling"]
+        out.update(
+            gb_per_s=round(per_step / (res["ms_per_step"] * 1e-3) / 1e9, 2),
+            tokens_per_s=round(plan.B / (res["ms_per_step"] * 1e-3), 1),
+            kv_tokens_per_layer=plan.kv_tokens(),
+            roofline=dict(bound="hbm", kernel=f"pkv_decode call (decode_kernel<{plan.d},"
+                                              f"{plan.H_q // plan.H_kv},...> + decode_merge_kernel)",
+                          achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                          frac=round(achieved / HBM_PEAK_GBS, 4), bytes_per_launch=per_call,
+                          read_ceiling=rc["gb_per_s"],
+                          frac_of_read_ceiling=round(achieved / rc["gb_per_s"], 4),
+                          read_ceiling_probe=rc))
+    else:
+        fl = prefill_flops(plan)
+        achieved = fl / med_s / 1e12
+        mc = ceilings["mfma_bf16"]["tflops"] if ceilings else None
+        out.update(
+            tokens_per_s=round(plan.total_new / (res["ms_per_step"] * 1e-3), 1),
+            roofline=dict(bound="mfma", kernel="prefill_kernel<128,2,4,true>",
+                          achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                          frac=round(achieved / BF16_PEAK_TFLOPS, 4), flops_per_launch=fl,
+                          mfma_ceiling=mc,
+                          frac_of_mfma_ceiling=None if mc is None else round(achieved / mc, 4)))
+    if "cpu" in res:
+        cpu = dict(res["cpu"])
+        if plan.kind == "decode":
+            cpu["gpu_speedup"] = round(out["roofline"]["achieved"] / cpu["value"], 1)
+        else:
+            cpu["gpu_speedup"] = round(achieved / cpu["value"], 1)
+        out["cpu_oracle"] = cpu
+    return out
 
-    import oracle as O
-    from workloads import make_plan, make_tensors
 
-    plan = make_plan(name)
-    tens = make_tensors(plan, "cpu", poison=False)
-    orc = O.default()
-    om = O.prepare_decode(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
-    scale = 1.0 / math.sqrt(plan.d)
-    reps, total = 0, 0.0
-    kc, vc = tens.k_cache().clone(), tens.v_cache().clone()
-    while total < budget_s and reps < 1000:
-        # storing the same rows again leaves the cache unchanged, so every
-        # repetition is the same full step
-        t0 = time.perf_counter()
-        orc.store(kc, vc, tens.k_new(), tens.v_new(), om["slot_mapping"])
-        orc.decode(tens.q[0], kc, vc, om["block_tables"], om["context_lens"], scale)
-        total += time.perf_counter() - t0
-        reps += 1
-    step_s = total / reps
-    gbs = (decode_bytes(plan) + store_bytes(plan)) / step_s / 1e9
-    log(f"cpu oracle: {reps} full steps of {name}, {step_s * 1e3:.1f} ms each, {orc.threads()} threads")
-    return dict(value=round(gbs, 3), unit="GB/s", cores=orc.threads(), kind="oracle",
-                sample=f"{reps} full {name} steps (store + decode of all {plan.B} sequences), "
-                       f"float64 C oracle, {step_s * 1e3:.1f} ms per step",
-                ms_per_step=round(step_s * 1e3, 2))
-
-
-def run_packed(steps, warmup, torch, pkv, log):
+def run_packed(steps, warmup, torch, pkv, log, ceilings):
     """Varlen causal prefill over packed K/V (no block table, no prefix): q/k/v
     are row views of one fused projection buffer."""
     from workloads.packed import PACKED_PREFILL as cfg, make_packed, split_fused
@@ -211,13 +422,19 @@ def run_packed(steps, warmup, torch, pkv, log):
     for _ in range(warmup):
         pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out)
     torch.cuda.synchronize()
-    ms = events_ms(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out),
-                   steps)
+    ms = timed_calls(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale,
+                                                                out=out), steps)
+    med = statistics.median(ms)
     fl = 4 * cfg["d"] * cfg["H_q"] * sum(causal_pairs(0, n) for n in lens)
-    tf = fl / (ms * 1e-3) / 1e12
-    return dict(workload="packed_prefill", B=cfg["B"], tokens=sum(lens), attn_ms=round(ms, 4),
-                prefill_tflops=round(tf, 2), prefill_pct_mfma_peak=round(100 * tf / BF16_PEAK_TFLOPS, 2),
-                tokens_per_s=round(sum(lens) / (ms * 1e-3), 1), flops=fl)
+    tf = fl / (med * 1e-3) / 1e12
+    mc = ceilings["mfma_bf16"]["tflops"] if ceilings else None
+    return dict(workload="packed_prefill", B=cfg["B"], tokens=sum(lens), attn_call_ms=spread(ms),
+                tokens_per_s=round(sum(lens) / (med * 1e-3), 1),
+                roofline=dict(bound="mfma", kernel="prefill_kernel<128,2,4,false>",
+                              achieved=round(tf, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                              frac=round(tf / BF16_PEAK_TFLOPS, 4), flops_per_launch=fl,
+                              mfma_ceiling=mc,
+                              frac_of_mfma_ceiling=None if mc is None else round(tf / mc, 4)))
 
 
 def run_graph(steps, warmup, torch, pkv, log):
@@ -332,8 +549,8 @@ def run_meta(steps, warmup, torch, pkv, log):
 
 def run_sample(steps, warmup, torch, pkv, log):
     """Gumbel-max sampling of one decode step: 256 rows of bf16 logits over a
-    151936-token vocabulary (pkv_sample_gumbel, both launches), HIP events on
-    the launch stream."""
+    151936-token vocabulary (pkv_sample_gumbel, both launches), a pair of HIP
+    events on the launch stream around every call."""
     from workloads.sampling import SAMPLE_DECODE as cfg, make_logits
 
     logits, temps, seeds, offsets = make_logits("cuda")
@@ -343,56 +560,30 @@ def run_sample(steps, warmup, torch, pkv, log):
     for _ in range(warmup):
         pkv.sample_gumbel(logits, seeds, temps, offsets, out=out, workspace=ws)
     torch.cuda.synchronize()
-    ms = events_ms(torch, lambda i: pkv.sample_gumbel(logits, seeds, temps, step_offsets[i], out=out,
-                                                      workspace=ws), steps)
+    calls = timed_calls(torch, lambda i: pkv.sample_gumbel(logits, seeds, temps, step_offsets[i],
+                                                           out=out, workspace=ws), steps)
+    ms = statistics.median(calls)
     n = cfg["B"] * cfg["V"]
     nbytes = 2 * n + cfg["B"] * (4 + 8 + 8 + 8)
     res = dict(workload="gumbel_sample", B=cfg["B"], V=cfg["V"], dtype="bf16", bound="alu",
-               ms=round(ms, 4),
+               ms=round(ms, 4), call_ms=spread(calls),
                logits_per_s=round(n / (ms * 1e-3), 1), gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 2),
                pct_hbm_peak=round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))
     log(f"gumbel_sample: {json.dumps(res)}")
     return res
 
 
-def copy_probe(torch, log, gib: float = 4.0, iters: int = 10) -> dict:
-    """Plain device copy (torch copy_) and plain read (torch sum) of a buffer of known
-    size: the achievable-bandwidth reference for the roofline, and the known-size
-    kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
-    n = int(gib * (1 << 30)) // 2
-    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
-    dst = torch.empty_like(src)
-    res = {}
-    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 4 * n),
-                             ("read", lambda: src.sum(), 2 * n)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / iters
-        res[name] = dict(bytes=nbytes, ms=round(ms, 4), gb_per_s=round(nbytes / ms / 1e6, 1))
-        log(f"{name} probe: {nbytes / 2**30:.2f} GiB in {ms:.3f} ms = {nbytes / ms / 1e6:.0f} GB/s")
-    return res
-
-
-SECONDARY = ("packed_prefill", "graph_decode", "device_metadata", "gumbel_sample",
-             "long_decode", "prefix_prefill", "full_step", "wide_gqa_decode")
+SECONDARY = ("qwen3_decode", "long_decode", "wide_gqa_decode", "prefix_prefill", "packed_prefill",
+             "graph_decode", "device_metadata", "gumbel_sample")
+ATTENTION = ("full_step", "qwen3_decode", "long_decode", "wide_gqa_decode", "prefix_prefill")
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3_decode",
-                    choices=["qwen3_decode", "long_decode", "prefix_prefill", "full_step",
-                             "wide_gqa_decode"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full_step", choices=list(ATTENTION))
     ap.add_argument("--pools", type=int, default=2,
                     help="independent copies of the cache rotated across steps (single-layer workloads)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -400,129 +591,102 @@ def main() -> int:
                     help="comma-separated secondary workloads to run (default: all of "
                          + ", ".join(SECONDARY) + ")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run the plain copy / read probes and print their JSON")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle compute for the headline workload's cpu_baseline")
+    ap.add_argument("--cpu-budget-secondary", type=float, default=2.0,
+                    help="seconds of oracle compute for each secondary attention workload")
+    ap.add_argument("--probes-only", action="store_true",
+                    help="only run the ceiling probes and print their JSON")
     args = ap.parse_args()
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this path has no "
-              "multi-GPU mode", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build measures the "
+              "path on one GPU and has no multi-GPU mode", file=sys.stderr)
         return 2
 
     import torch
 
     import paged_kv_cache_110_amd as pkv
+    from paged_kv_cache_110_amd import probe
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     pkv._lib.load()
-    if args.copy_probe:
-        print(json.dumps(dict(probe=copy_probe(torch, log))), flush=True)
+    probe.load()
+    ceilings = measure_ceilings(torch, probe, log)
+    if args.probes_only:
+        print(json.dumps(dict(ceilings=ceilings)), flush=True)
         return 0
 
-    def summarize(res):
-        plan = res["plan"]
-        out = dict(workload=plan.name, ms_per_step=round(res["ms_per_step"], 4),
-                   attn_ms=round(res["attn_ms"], 4), store_ms=round(res["store_ms"], 4))
-        if plan.kind == "decode":
-            db = decode_bytes(plan) * plan.layers
-            sb = store_bytes(plan) * plan.layers
-            out["gb_per_s"] = round((db + sb) / (res["ms_per_step"] * 1e-3) / 1e9, 2)
-            out["decode_gb_per_s"] = round(decode_bytes(plan) / (res["attn_ms"] * 1e-3) / 1e9, 2)
-            out["decode_pct_hbm_peak"] = round(100 * out["decode_gb_per_s"] / HBM_PEAK_GBS, 2)
-            out["tokens_per_s"] = round(plan.B / (res["ms_per_step"] * 1e-3), 1)
-            out["kv_tokens_per_layer"] = plan.kv_tokens()
-        else:
-            fl = prefill_flops(plan)
-            out["prefill_tflops"] = round(fl / (res["attn_ms"] * 1e-3) / 1e12, 2)
-            out["prefill_pct_mfma_peak"] = round(100 * out["prefill_tflops"] / BF16_PEAK_TFLOPS, 2)
-            out["tokens_per_s"] = round(plan.total_new / (res["ms_per_step"] * 1e-3), 1)
-            out["flops"] = fl
-        return out
-
-    main_res = run_workload(args.workload, args.steps, args.warmup,
-                            args.pools if args.workload != "full_step" else 1, torch, pkv, log)
-    plan = main_res["plan"]
-    s = summarize(main_res)
-    log(json.dumps(s))
-
-    secondary = {}
     wanted = set() if args.no_secondary else (
         set(SECONDARY) if args.secondary == "all" else set(args.secondary.split(",")))
     unknown = wanted - set(SECONDARY)
     if unknown:
         print(f"unknown secondary workloads: {sorted(unknown)}", file=sys.stderr)
         return 2
-    if wanted:
-        n2 = max(5, args.steps // 2)
-        if "packed_prefill" in wanted:
-            secondary["packed_prefill"] = run_packed(n2, 2, torch, pkv, log)
-            log(json.dumps(secondary["packed_prefill"]))
-        if "graph_decode" in wanted:
-            secondary["graph_decode"] = run_graph(n2, 3, torch, pkv, log)
-        if "device_metadata" in wanted:
-            secondary["device_metadata"] = run_meta(n2, 3, torch, pkv, log)
-        if "gumbel_sample" in wanted:
-            secondary["gumbel_sample"] = run_sample(n2, 3, torch, pkv, log)
-        for name in ["long_decode", "prefix_prefill", "full_step", "wide_gqa_decode"]:
-            if name == args.workload or name not in wanted:
-                continue
-            r = run_workload(name, max(5, args.steps // 2), 2,
-                             1 if name in ("full_step", "prefix_prefill") else args.pools,
-                             torch, pkv, log)
-            secondary[name] = summarize(r)
-            log(json.dumps(secondary[name]))
 
+    def pools_of(name):
+        return 1 if name in ("full_step", "prefix_prefill") else args.pools
+
+    cpu_b = None if args.no_cpu_baseline else args.cpu_budget
+    main_res = run_workload(args.workload, args.steps, args.warmup, pools_of(args.workload), torch,
+                            pkv, probe, log, cpu_budget=cpu_b)
+    plan = main_res["plan"]
+    s = summarize(main_res, ceilings)
+    log(json.dumps({k: v for k, v in s.items() if k != "roofline"}))
+
+    secondary = {}
+    n2 = max(5, args.steps)
+    cpu2 = None if args.no_cpu_baseline else args.cpu_budget_secondary
+    for name in ATTENTION:
+        if name == args.workload or name not in wanted:
+            continue
+        r = run_workload(name, n2, 2, pools_of(name), torch, pkv, probe, log, cpu_budget=cpu2)
+        secondary[name] = summarize(r, ceilings)
+        log(json.dumps(secondary[name]))
+    if "packed_prefill" in wanted:
+        secondary["packed_prefill"] = run_packed(n2, 2, torch, pkv, log, ceilings)
+        log(json.dumps(secondary["packed_prefill"]))
+    if "graph_decode" in wanted:
+        secondary["graph_decode"] = run_graph(n2, 3, torch, pkv, log)
+    if "device_metadata" in wanted:
+        secondary["device_metadata"] = run_meta(n2, 3, torch, pkv, log)
+    if "gumbel_sample" in wanted:
+        secondary["gumbel_sample"] = run_sample(n2, 3, torch, pkv, log)
+
+    roofline = dict(s["roofline"])
     if plan.kind == "decode":
-        value = s["gb_per_s"]
-        unit = "GB/s"
-        per_launch = decode_bytes(plan)
-        achieved = per_launch / (main_res["attn_ms"] * 1e-3) / 1e9
+        value, unit = s["gb_per_s"], "GB/s"
         traffic = measured_traffic(plan.name)
-        roofline = dict(bound="hbm", kernel="pkv_decode call (decode_kernel + decode_merge_kernel)",
-                        achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4),
-                        traffic=None if traffic is None else round(traffic),
-                        traffic_unit="bytes per call (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
-                        bytes_per_launch=per_launch, avg_launch_ms=round(main_res["attn_ms"], 4))
+        roofline.update(
+            traffic=None if traffic is None else round(traffic),
+            traffic_unit="HBM bytes per call (FETCH_SIZE x f + WRITE_SIZE x w, factors from the "
+                         "probe copy kernel)",
+            avg_launch_ms=s["attn_call_ms"]["mean"], launch_ms=s["attn_call_ms"],
+            copy_ceiling=ceilings["copy"]["gb_per_s"], plain_read_ceiling=ceilings["read"]["gb_per_s"])
     else:
-        value = s["prefill_tflops"]
-        unit = "TFLOP/s"
-        fl = prefill_flops(plan)
-        achieved = fl / (main_res["attn_ms"] * 1e-3) / 1e12
-        roofline = dict(bound="mfma", kernel="prefill_kernel", achieved=round(achieved, 2),
-                        peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
-                        flops_per_launch=fl, avg_launch_ms=round(main_res["attn_ms"], 4))
-
-    if plan.kind == "decode":
-        # the same bytes against what plain torch kernels stream on this device
-        probe = copy_probe(torch, log, gib=2.0, iters=5)
-        torch.cuda.empty_cache()
-        roofline["copy_ceiling_gb_per_s"] = probe["copy"]["gb_per_s"]
-        roofline["read_ceiling_gb_per_s"] = probe["read"]["gb_per_s"]
-        roofline["frac_of_copy"] = round(achieved / probe["copy"]["gb_per_s"], 4)
-        roofline["frac_of_read"] = round(achieved / probe["read"]["gb_per_s"], 4)
-
+        value, unit = s["roofline"]["achieved"], "TFLOP/s"
+        roofline.update(traffic=None, avg_launch_ms=s["attn_call_ms"]["mean"],
+                        launch_ms=s["attn_call_ms"])
     cpu = None
-    if not args.no_cpu_baseline and plan.kind == "decode" and args.workload != "full_step":
-        cpu = cpu_baseline(args.workload, args.cpu_budget, log)
+    if "cpu_oracle" in s:
+        cpu = s["cpu_oracle"]
 
     config = dict(workload=plan.name, B=plan.B, H_q=plan.H_q, H_kv=plan.H_kv, d=plan.d,
                   block_size=plan.block_size, layers=plan.layers, num_blocks=plan.num_blocks,
                   kv_tokens=plan.kv_tokens(), new_tokens=plan.total_new,
-                  pools_rotated=args.pools if args.workload != "full_step" else 1,
+                  pools_rotated=pools_of(plan.name),
                   step="store + attention" + (" per layer" if plan.layers > 1 else ""))
+    detail = {k: v for k, v in s.items() if k not in ("roofline", "cpu_oracle")}
     line = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps,
                 warmup=args.warmup, ms_per_step=s["ms_per_step"], higher_is_better=True,
                 scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-                config=config, roofline=roofline, cpu_baseline=cpu, detail=s,
-                secondary=secondary)
+                config=config, roofline=roofline, cpu_baseline=cpu, detail=detail,
+                ceilings=ceilings, secondary=secondary)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -1,4 +1,5 @@
-"""Build libpkv.so in-tree with hipcc for gfx950.
+"""Build libpkv.so (the attention library) and libpkv_probe.so (the
+benchmark's measurement probes) in-tree with hipcc for gfx950.
 
 Usage: python -m paged_kv_cache_110_amd.build
 """
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
+PROBE_SOURCES = ["pkv_probe.hip"]
 SOURCES = ["pkv_api.cpp", "pkv_graph.cpp", "pkv_store.hip", "pkv_meta.hip", "pkv_sample.hip", "pkv_decode.hip", "pkv_prefill.hip"]
 HEADERS = ["decode_schedule.h", "device_common.h", "pkv_internal.h"]
 
@@ -45,19 +48,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpkv.so next to this file; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{res.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpkv.so and libpkv_probe.so next to this
+    file; returns the path of libpkv.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -334,3 +334,44 @@ def test_sample_argument_checks_before_any_hip_call():
     assert lib.pkv_sample_workspace_size(2, 100) == 16
     assert lib.pkv_sample_workspace_size(3, 151936) == 3 * 38 * 8
     assert lib.pkv_sample_workspace_size(0, 10) == 0
+
+
+def test_probe_library_exports_and_argument_checks():
+    """libpkv_probe.so (the benchmark's ceiling probes) loads, exports what
+    include/pkv_probe.h declares, and rejects bad arguments before any HIP call."""
+    from paged_kv_cache_110_amd import probe
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_probe.h")).read(),
+                  flags=re.S)
+    declared = sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+    assert declared == sorted(probe.EXPORTS)
+    lib = probe.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    buf = ctypes.create_string_buffer(4096 + 16)
+    p = (ctypes.addressof(buf) + 15) // 16 * 16
+    # paged read: d, block size, null pointers, empty page list, misaligned cache
+    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 8, 96, 256, p, None) == 1
+    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 8, 128, 48, p, None) == 1
+    assert lib.pkv_probe_paged_read(None, p, p, 1, 4, 8, 128, 256, p, None) == 1
+    assert lib.pkv_probe_paged_read(p, p, p, 0, 4, 8, 128, 256, p, None) == 1
+    assert lib.pkv_probe_paged_read(p + 2, p, p, 1, 4, 8, 128, 256, p, None) == 1
+    # read / copy: sizes that are not whole 16-byte chunks, misaligned buffers
+    assert lib.pkv_probe_read(p, 24, p, 0, None) == 1
+    assert lib.pkv_probe_read(p + 8, 32, p, 0, None) == 1
+    assert lib.pkv_probe_copy(p, p, 0, 0, None) == 1
+    assert lib.pkv_probe_copy(p + 4, p, 32, 0, None) == 1
+    # mfma: chain counts and occupancies outside the supported set
+    assert lib.pkv_probe_mfma(p, 256, 2, 10, 3, 0, None) == 1
+    assert lib.pkv_probe_mfma(p, 256, 9, 10, 4, 0, None) == 1
+    assert lib.pkv_probe_mfma(None, 256, 2, 10, 4, 0, None) == 1
+
+
+def test_probe_page_list():
+    """The probe's page list holds one (physical block, tokens used) pair per
+    page a decode reads: whole pages, then the remainder of the last."""
+    from paged_kv_cache_110_amd.probe import pages_of
+
+    bt = torch.tensor([[5, 2, -1], [7, -1, -1], [1, 3, 4]], dtype=torch.int32)
+    cl = torch.tensor([17, 16, 33], dtype=torch.int32)
+    assert pages_of(bt, cl, 16).tolist() == [[5, 16], [2, 1], [7, 16], [1, 16], [3, 16], [4, 1]]
