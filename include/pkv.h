@@ -56,7 +56,8 @@ typedef enum pkv_status {
   PKV_OK = 0,
   PKV_EINVAL = 1,       /* an argument violates a documented constraint */
   PKV_EUNSUPPORTED = 2, /* valid, but not a shape this build has kernels for */
-  PKV_ELAUNCH = 3       /* the HIP runtime reported an error at launch */
+  PKV_ELAUNCH = 3,      /* the HIP runtime reported an error at launch */
+  PKV_ESCRATCH = 4      /* more scratch than pkv_sample_gumbel_noalloc's fixed array holds */
 } pkv_status;
 
 /* Static, human-readable name of a status code. */
@@ -282,6 +283,30 @@ pkv_status pkv_sample_gumbel(int64_t* tokens, const void* logits, int32_t logits
                              const float* temperatures, const int64_t* seeds,
                              const int64_t* offsets, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * pkv_sample_gumbel without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, draws and results as
+ * pkv_sample_gumbel (the same kernels, bit-identical tokens); the chunk keys
+ * go to a fixed scratch array inside the library instead of a workspace:
+ * 2^17 keys of 8 bytes (1 MiB) per device, held from the library's first use
+ * on that device until the process ends.  The first call on each device
+ * looks up that device's copy (no allocation); nothing in it needs clearing,
+ * since every key a call reads is written by the same call.
+ * Limit: B * ceil(V / chunk) <= 131072 keys, chunk = 8192 logits for bf16 and
+ * 4096 for fp32 (e.g. V = 151936: B <= 6898 bf16, B <= 3449 fp32); larger
+ * calls return PKV_ESCRATCH and enqueue nothing.
+ * Every call on one device shares that device's array: calls that can
+ * overlap on one device (other streams, other host threads) race and give
+ * unspecified tokens; keep them in one stream's order.
+ * Errors as for pkv_sample_gumbel (without the workspace checks), plus
+ * PKV_ESCRATCH, and PKV_ELAUNCH if the scratch address cannot be found.
+ */
+pkv_status pkv_sample_gumbel_noalloc(int64_t* tokens, const void* logits, int32_t logits_bf16,
+                                     int64_t row_stride, int32_t B, int32_t V,
+                                     const float* temperatures, const int64_t* seeds,
+                                     const int64_t* offsets, hipStream_t stream);
 
 /*
  * Staged row writes into a device int32 table (docs.vllm.com.cn, "Model

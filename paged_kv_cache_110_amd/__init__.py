@@ -19,6 +19,7 @@ Functions:
     StagedWrites(table): stage_write(row, start, values), apply()
     prepare_metadata_device(idx_mapping, num_computed, num_scheduled, block_table, ...) -> dict
     sample_gumbel(logits, seeds, temperatures=None, offsets=None) -> int64 tokens
+    sample_gumbel_noalloc(logits, seeds, temperatures=None, offsets=None, out=None) -> int64 tokens
     graph_bucket(max_batch, batch) -> int
     DecodeGraph(k_caches, v_caches, max_batch, H_q, max_blocks_per_seq, ...)
 """
@@ -36,7 +37,8 @@ from ._lib import EXPORTS, LIB_PATH, DecodeStep, PkvError, check, load
 __all__ = [
     "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
     "prefill_varlen_packed", "pack_row_writes", "apply_row_writes", "StagedWrites",
-    "prepare_metadata_device", "sample_gumbel", "sample_workspace_size", "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
+    "prepare_metadata_device", "sample_gumbel", "sample_gumbel_noalloc", "sample_workspace_size",
+    "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
     "version",
 ]
 
@@ -370,6 +372,35 @@ def sample_gumbel(logits: torch.Tensor, seeds: torch.Tensor,
     check("pkv_sample_gumbel", load().pkv_sample_gumbel(
         _ptr(out), _ptr(logits), int(logits.dtype == torch.bfloat16), logits.stride(0), B, V,
         _ptr(temperatures), _ptr(seeds), _ptr(offsets), _ptr(workspace), have, _stream(stream)))
+    return out
+
+
+def sample_gumbel_noalloc(logits: torch.Tensor, seeds: torch.Tensor,
+                          temperatures: Optional[torch.Tensor] = None,
+                          offsets: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sample_gumbel without a workspace (pkv_sample_gumbel_noalloc): the
+    library's fixed per-device scratch holds the chunk keys.  Pass ``out`` to
+    allocate nothing at all.  Returns int64 tokens [B]."""
+    _need(logits.is_cuda and logits.dim() == 2 and logits.stride(1) == 1
+          and logits.dtype in (torch.bfloat16, torch.float32),
+          "logits must be a GPU bf16/fp32 [B, V] tensor with unit stride along V")
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    _need(seeds.is_cuda and seeds.dtype == torch.int64 and seeds.shape == (B,)
+          and seeds.is_contiguous(), "seeds must be a contiguous GPU int64 [B] tensor")
+    if offsets is not None:
+        _need(offsets.is_cuda and offsets.dtype == torch.int64 and offsets.shape == (B,)
+              and offsets.is_contiguous(), "offsets must be a contiguous GPU int64 [B] tensor")
+    if temperatures is not None:
+        _need(temperatures.is_cuda and temperatures.dtype == torch.float32
+              and temperatures.shape == (B,) and temperatures.is_contiguous(),
+              "temperatures must be a contiguous GPU fp32 [B] tensor")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int64, device=logits.device)
+    _need(out.dtype == torch.int64 and out.shape == (B,) and out.is_contiguous(), "bad out")
+    check("pkv_sample_gumbel_noalloc", load().pkv_sample_gumbel_noalloc(
+        _ptr(out), _ptr(logits), int(logits.dtype == torch.bfloat16), logits.stride(0), B, V,
+        _ptr(temperatures), _ptr(seeds), _ptr(offsets), _stream(stream)))
     return out
 
 

@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
-PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH = 0, 1, 2, 3
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ELAUNCH, PKV_ESCRATCH = 0, 1, 2, 3, 4
 
 # every symbol include/pkv.h declares
 EXPORTS = (
@@ -25,6 +25,7 @@ EXPORTS = (
     "pkv_prefill_varlen_packed",
     "pkv_sample_workspace_size",
     "pkv_sample_gumbel",
+    "pkv_sample_gumbel_noalloc",
     "pkv_pack_row_writes",
     "pkv_apply_row_writes",
     "pkv_prepare_metadata_device",
@@ -97,6 +98,8 @@ def load() -> ctypes.CDLL:
     lib.pkv_sample_workspace_size.restype = SZ
     lib.pkv_sample_gumbel.argtypes = [P, P, I32, I64, I32, I32, P, P, P, P, SZ, P]
     lib.pkv_sample_gumbel.restype = ctypes.c_int
+    lib.pkv_sample_gumbel_noalloc.argtypes = [P, P, I32, I64, I32, I32, P, P, P, P]
+    lib.pkv_sample_gumbel_noalloc.restype = ctypes.c_int
     lib.pkv_pack_row_writes.argtypes = [I32, P, P, P, P, I32, I32, P, I64, P]
     lib.pkv_pack_row_writes.restype = ctypes.c_int
     lib.pkv_apply_row_writes.argtypes = [P, I64, I32, I32, P, I32, I32, P]

@@ -64,6 +64,9 @@ const char* pkv_status_string(int status) {
     case PKV_EINVAL: return "PKV_EINVAL: invalid argument";
     case PKV_EUNSUPPORTED: return "PKV_EUNSUPPORTED: unsupported head size or group size";
     case PKV_ELAUNCH: return "PKV_ELAUNCH: kernel launch failed";
+    case PKV_ESCRATCH:
+      return "PKV_ESCRATCH: the call needs more scratch than the fixed array of the "
+             "no-allocation entry point holds";
     default: return "unknown pkv status";
   }
 }
@@ -327,6 +330,23 @@ pkv_status pkv_sample_gumbel(int64_t* tokens, const void* logits, int32_t logits
   if (workspace_bytes < pkv_sample_workspace_size(B, V)) return PKV_EINVAL;
   return launch_status(pkv::launch_sample(tokens, logits, logits_bf16 != 0, row_stride, B, V,
                                           temperatures, seeds, offsets, workspace, stream));
+}
+
+pkv_status pkv_sample_gumbel_noalloc(int64_t* tokens, const void* logits, int32_t logits_bf16,
+                                     int64_t row_stride, int32_t B, int32_t V,
+                                     const float* temperatures, const int64_t* seeds,
+                                     const int64_t* offsets, hipStream_t stream) {
+  if (B < 0 || V < 1 || row_stride < V) return PKV_EINVAL;
+  if (row_stride % (logits_bf16 ? 8 : 4) != 0) return PKV_EINVAL;
+  if (B == 0) return PKV_OK;
+  if (!tokens || !logits || !seeds || !aligned16(logits)) return PKV_EINVAL;
+  if (B > 65535) return PKV_EINVAL;  // one grid row per batch row
+  const int64_t chunk = pkv::sample_chunk_size(logits_bf16 != 0);
+  if ((int64_t)B * ((V + chunk - 1) / chunk) > pkv::kSampleScratchKeys) return PKV_ESCRATCH;
+  void* scratch = nullptr;
+  if (pkv::sample_scratch_address(&scratch) != hipSuccess) return PKV_ELAUNCH;
+  return launch_status(pkv::launch_sample(tokens, logits, logits_bf16 != 0, row_stride, B, V,
+                                          temperatures, seeds, offsets, scratch, stream));
 }
 
 }  // extern "C"

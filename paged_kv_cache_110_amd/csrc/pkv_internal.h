@@ -41,6 +41,13 @@ hipError_t launch_sample(int64_t* tokens, const void* logits, bool bf16, int64_t
                          int32_t B, int32_t V, const float* temps, const int64_t* seeds,
                          const int64_t* offsets, void* workspace, hipStream_t stream);
 
+// The no-allocation sampling entry point's fixed scratch: this many 8-byte
+// chunk keys (1 MiB) per device, in a file-scope device array of
+// pkv_sample.hip.  sample_scratch_address gives the current device's copy
+// (looked up once per device, under a lock).
+constexpr int64_t kSampleScratchKeys = (int64_t)1 << 17;
+hipError_t sample_scratch_address(void** address);
+
 // Decode launch plan: one wavefront per resident slot of the current device.
 struct DecodePlan {
   int32_t num_waves;       // 0 when the shape has no kernel

@@ -15,12 +15,42 @@
 // keys and its best key goes to the workspace.
 // sample_reduce_kernel: one wavefront per row takes the best chunk key and
 // writes the token.  Keys order by score, then by smaller index.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
 #include "pkv_internal.h"
 
+// Fixed scratch of the no-allocation entry point: the chunk keys of one call
+// (kSampleScratchKeys x 8 bytes), one copy per device, held until the process
+// ends.  Host code must never pass this name to a kernel: on the host it is a
+// stand-in, not the device address, which sample_scratch_address looks up.
+static __device__ __align__(256) uint64_t scratch[pkv::kSampleScratchKeys];
+
 namespace pkv {
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxScratchDevices];  // per device, set on first use
+}  // namespace
+
+hipError_t sample_scratch_address(void** address) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_address[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_address[dev] = p;
+  }
+  *address = g_scratch_address[dev];
+  return hipSuccess;
+}
 
 constexpr int kSampleThreads = 256;
 constexpr int kSampleSteps = 4;  // 16-byte loads per thread per chunk

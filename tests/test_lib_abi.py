@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib.load()
-    for code in range(4):
+    for code in range(5):
         assert lib.pkv_status_string(code).decode().startswith("PKV_")
     assert b"unknown" in lib.pkv_status_string(99)
 
@@ -375,3 +375,20 @@ def test_probe_page_list():
     bt = torch.tensor([[5, 2, -1], [7, -1, -1], [1, 3, 4]], dtype=torch.int32)
     cl = torch.tensor([17, 16, 33], dtype=torch.int32)
     assert pages_of(bt, cl, 16).tolist() == [[5, 16], [2, 1], [7, 16], [1, 16], [3, 16], [4, 1]]
+
+
+def test_sample_noalloc_refuses_sizes_beyond_its_scratch():
+    """pkv_sample_gumbel_noalloc: the fixed scratch holds 2^17 chunk keys;
+    larger calls return PKV_ESCRATCH on the host, before any HIP call."""
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(4096 + 16)
+    p = (ctypes.addressof(buf) + 15) // 16 * 16
+    V = 151936
+    # bf16 chunks are 8192 logits (19 per row), fp32 chunks 4096 (38 per row)
+    assert lib.pkv_sample_gumbel_noalloc(p, p, 1, V, 6899, V, None, p, None, None) == _lib.PKV_ESCRATCH
+    assert lib.pkv_sample_gumbel_noalloc(p, p, 0, V, 3450, V, None, p, None, None) == _lib.PKV_ESCRATCH
+    assert lib.pkv_sample_gumbel_noalloc(p, p, 1, V, 65536, V, None, p, None, None) == _lib.PKV_EINVAL
+    assert lib.pkv_sample_gumbel_noalloc(p, p, 1, V, 0, V, None, p, None, None) == 0  # nothing to do
+    assert lib.pkv_sample_gumbel_noalloc(None, p, 1, V, 4, V, None, p, None, None) == _lib.PKV_EINVAL
+    assert lib.pkv_sample_gumbel_noalloc(p, p + 2, 1, V, 4, V, None, p, None, None) == _lib.PKV_EINVAL
+    assert lib.pkv_sample_gumbel_noalloc(p, p, 1, V - 1, 4, V, None, p, None, None) == _lib.PKV_EINVAL
