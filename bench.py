@@ -388,6 +388,12 @@ def summarize(res, ceilings) -> dict:
                           read_ceiling=rc["gb_per_s"],
                           frac_of_read_ceiling=round(achieved / rc["gb_per_s"], 4),
                           read_ceiling_probe=rc))
+        traffic = measured_traffic(plan.name)
+        out["roofline"].update(
+            traffic=None if traffic is None else round(traffic),
+            traffic_unit="HBM bytes per call: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from the "
+                         "probe copy kernel), profiles/traffic.json; null when unmeasured or when the "
+                         "decode source changed since")
     else:
         fl = prefill_flops(plan)
         achieved = fl / med_s / 1e12
@@ -661,11 +667,7 @@ def main() -> int:
     roofline = dict(s["roofline"])
     if plan.kind == "decode":
         value, unit = s["gb_per_s"], "GB/s"
-        traffic = measured_traffic(plan.name)
         roofline.update(
-            traffic=None if traffic is None else round(traffic),
-            traffic_unit="HBM bytes per call (FETCH_SIZE x f + WRITE_SIZE x w, factors from the "
-                         "probe copy kernel)",
             avg_launch_ms=s["attn_call_ms"]["mean"], launch_ms=s["attn_call_ms"],
             copy_ceiling=ceilings["copy"]["gb_per_s"], plain_read_ceiling=ceilings["read"]["gb_per_s"])
     else:
