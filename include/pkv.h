@@ -183,10 +183,14 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
  *   max_seqlen_k  host bound on nk (informational; keys are clamped to the table)
  *   other arguments as for pkv_decode.
  * Query rows at or beyond total_q are never written.
- * Precision: q.k products and all sums in fp32; the probabilities and V enter
- * the PV product as fp16, so every V value must lie within fp16's range
- * (|v| <= 65504; larger values give non-finite rows); V values under 2^-14 in
- * magnitude are rounded to fp16 subnormals (absolute error below 2^-25).
+ * Precision: q.k products and all sums in fp32.  Every finite bf16 V is
+ * accepted: the probabilities and V first enter the PV product as fp16; a
+ * workgroup whose rows come out non-finite (a V value beyond fp16's range,
+ * |v| >= 2^16) or all below 2^-14 in magnitude (where fp16 subnormals of tiny
+ * V values would show) computes its tiles again with V in bf16 and the
+ * probabilities split into bf16 high and low parts (about 2^-16 relative).
+ * As in pkv_decode, the fp32 sums bound the result: sum_j p_j |v_j| with
+ * max_j p_j = 1 must stay below fp32's largest value.
  * PKV_EINVAL / PKV_EUNSUPPORTED as for pkv_decode, plus total_q < 0,
  * max_seqlen_q < 0, B > 65535 or a softmax_scale that is not finite and
  * positive (PKV_EINVAL), and max_seqlen_q above
@@ -222,7 +226,7 @@ pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,
  *   max_seqlen_k  host bound on nk (informational)
  * Key rows outside [0, total_k) are never read (rows are clamped; the results
  * of calls that violate the cu_seqlens preconditions are unspecified).
- * Precision as for pkv_prefill_varlen (V within fp16's range).
+ * Precision as for pkv_prefill_varlen (every finite bf16 V).
  * PKV_EINVAL: null pointers, non-positive sizes, H_q % H_kv != 0, a stride
  * below the row size or not a multiple of 8, misaligned pointers, B < 0,
  * B > 65535, total_q < 0, total_k < 0, total_k == 0 with work to do, or a

@@ -30,7 +30,10 @@
 //    (bf16 would leave outputs of magnitude 2..4 close to the 1e-2 error
 //    bar), and the V^T operand comes straight from the row-major V tile, kept
 //    in LDS as fp16 (exact for bf16 values of normal fp16 range), with
-//    ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit elements;
+//    ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit elements.
+//    A workgroup whose rows show that V left fp16's range (a non-finite row,
+//    or a row whose outputs are all tiny) runs its tiles again with V in bf16
+//    and P as bf16 high and low parts, so every finite bf16 V is served;
 //  - online softmax in the log2 domain with the same lazy rescale as decode;
 //    only tiles that cross the diagonal are masked;
 //  - grid (KV head, query tile, sequence), so the dispatch order is sequence
@@ -276,20 +279,22 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
       full_next = false;
     }
   };
-  auto stash_tile = [&](uint16_t* kt_lds, uint16_t* vt_lds) {
+  // V goes to LDS as fp16 (the fast pass) or unchanged as bf16 (the exact pass).
+  auto stash_tile = [&](uint16_t* kt_lds, uint16_t* vt_lds, auto exact_tag) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
+    auto vconv = [](u32x4 w) { return EXACT ? w : bf16x8_to_f16x8(w); };
     if (full_next) {
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         *reinterpret_cast<u32x4*>(kt_lds + soff + RPP * p * D) = kr[p];
-        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = bf16x8_to_f16x8(vr[p]);
+        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = vconv(vr[p]);
       }
     } else {
       const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         *reinterpret_cast<u32x4*>(kt_lds + soff + RPP * p * D) = kok[p] ? kr[p] : zero;
-        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) =
-            kok[p] ? bf16x8_to_f16x8(vr[p]) : zero;
+        *reinterpret_cast<u32x4*>(vt_lds + soff + RPP * p * D) = kok[p] ? vconv(vr[p]) : zero;
       }
     }
   };
@@ -309,7 +314,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
       }
     }
   };
-  auto softmax = [&](int kt, f32x16 (&sacc)[2], f16x8 (&pf)[2][2]) {
+  // Mask, running max and rescale of one tile's scores.  The fast pass
+  // rescales lazily (P up to 2^8); the exact pass whenever the maximum grows
+  // (P up to 1, so P * V stays within fp32 for every finite bf16 V).
+  auto softmax_max = [&](int kt, f32x16 (&sacc)[2], float lazy) {
     // causal mask, only on tiles that reach past this wavefront's first position
     if (kt * BN + BN - 1 > wave_first_pos) {
 #pragma unroll
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx *= scale_log2e;  // the scale is positive: max commutes with it
     mx = cross_reduce<32, true>(mx);  // with lane l ^ 32, on the VALU (v_permlane32_swap)
-    if (__any(mx > m + kPrefillLazy)) {
+    if (__any(mx > m + lazy)) {
       const float mn = fmaxf(m, mx);
       const float alpha = fast_exp2(m - mn);
       m = mn;
@@ -335,6 +343,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
+  };
+  auto softmax = [&](int kt, f32x16 (&sacc)[2], f16x8 (&pf)[2][2]) {
+    softmax_max(kt, sacc, kPrefillLazy);
     // P = 2^(s * scale * log2 e - m) (at most 2^8 with the lazy rescale),
     // rounded to fp16 for the PV product
 #pragma unroll
@@ -347,6 +358,17 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
           l += p;
           pf[kb][s2][e] = (_Float16)p;
         }
+  };
+  auto softmax_exact = [&](int kt, f32x16 (&sacc)[2]) {
+    softmax_max(kt, sacc, 0.0f);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(sacc[kb][r], scale_log2e, -m));
+        l += p;
+        sacc[kb][r] = p;  // kept in fp32 until the PV product splits it
+      }
   };
   auto pv_mfma = [&](const uint16_t* vt_lds, const f16x8 (&pf)[2][2]) {
     // key slice outermost: the four d blocks' MFMAs of one slice are
@@ -367,15 +389,45 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
         }
   };
 
-  load_tile(0);
-  stash_tile(lds, lds + TILE);
-  __syncthreads();
+  // The exact pass's PV product: V in bf16 as stored, P split into bf16 high
+  // and low parts (P to about 2^-16 relative), two MFMAs per slice and block.
+  auto pv_mfma_exact = [&](const uint16_t* vt_lds, const f32x16 (&pacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = pacc[kb][8 * s2 + e];
+          ph[e] = (__bf16)p;
+          pl[e] = (__bf16)(p - (float)ph[e]);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int rofs = (kb * 32 + 16 * s2) * D;
+          const i16x4 va = lds_read_tr16(vt_lds + (voff[0] ^ (32 * db)) + rofs);
+          const i16x4 vb = lds_read_tr16(vt_lds + (voff[1] ^ (32 * db)) + rofs);
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+          const bf16x8 vv = __builtin_bit_cast(bf16x8, v8);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, ph, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pl, o[db], 0, 0, 0);
+        }
+      }
+  };
+
+  // Set when a fast pass produced a non-finite row of this workgroup.
+  __shared__ int redo_exact;
+  if (tid == 0) redo_exact = 0;  // ordered before the reads by the loop's barriers
+
   // Tile kt computes from LDS buffer kt & 1 and stages tile kt + 1 into the
   // other.  The loop runs two tiles per iteration so that each buffer's base
   // is a constant: the LDS operand addresses are then loop-invariant
   // registers plus immediate offsets.
-  auto tile_step = [&](int kt, auto buf_tag) {
+  auto tile_step = [&](int kt, auto buf_tag, auto exact_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool EXACT = decltype(exact_tag)::value;
     uint16_t* cur = lds + BUF * 2 * TILE;
     uint16_t* nxt = lds + (1 - BUF) * 2 * TILE;
     const bool more = kt + 1 < ntiles;
@@ -384,17 +436,62 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
     // its rows: it would add nothing, so only the loading is shared
     if (kt * BN <= wave_last_pos) {
       f32x16 sacc[2];
-      f16x8 pf[2][2];
       score_mfma(cur, sacc);
-      softmax(kt, sacc, pf);
-      pv_mfma(cur + TILE, pf);
+      if constexpr (EXACT) {
+        softmax_exact(kt, sacc);
+        pv_mfma_exact(cur + TILE, sacc);
+      } else {
+        f16x8 pf[2][2];
+        softmax(kt, sacc, pf);
+        pv_mfma(cur + TILE, pf);
+      }
     }
-    if (more) stash_tile(nxt, nxt + TILE);
+    if (more) stash_tile(nxt, nxt + TILE, exact_tag);
     __syncthreads();
   };
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    tile_step(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < ntiles) tile_step(kt + 1, std::integral_constant<int, 1>{});
+  auto run_pass = [&](auto exact_tag) {
+    load_tile(0);
+    stash_tile(lds, lds + TILE, exact_tag);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile_step(kt, std::integral_constant<int, 0>{}, exact_tag);
+      if (kt + 1 < ntiles) tile_step(kt + 1, std::integral_constant<int, 1>{}, exact_tag);
+    }
+  };
+
+  run_pass(std::false_type{});
+  // The fast pass holds V in fp16.  Two cases need the exact pass instead:
+  //  - a V value beyond fp16's range (|v| >= 2^16) becomes an fp16 infinity,
+  //    and every row whose PV product met it ends non-finite (an infinity, or
+  //    a NaN from an infinity times a zero weight);
+  //  - V values below fp16's normal range (2^-14) keep an absolute error of
+  //    up to 2^-25, which is below a bf16 output's rounding only while the
+  //    row's largest output is at least about 2^-14.
+  // If any row of the workgroup (which shares the tiles in LDS) has either,
+  // the whole workgroup runs again exactly: V in bf16, P in two bf16 parts.
+  // Checked once per row, after the tile loop.
+  {
+    float chk = l, amax = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        chk += o[db][r];
+        amax = fmaxf(amax, fabsf(o[db][r]));
+      }
+    // the row's other half (d values and keys) sits in lane l ^ 32
+    const float row_l = l + shfl_xor_f32(l, 32);
+    const float row_amax = fmaxf(amax, shfl_xor_f32(amax, 32));
+    const bool small = row_ok && !(row_amax >= 0x1p-14f * row_l);
+    if (__any(!__builtin_isfinite(chk) || small) && lane == 0) redo_exact = 1;
+    __syncthreads();
+    if (redo_exact) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+      m = kNegSentinel;
+      l = 0.f;
+      run_pass(std::true_type{});
+    }
   }
 
   l += shfl_xor_f32(l, 32);

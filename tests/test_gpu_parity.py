@@ -325,3 +325,70 @@ def test_full_size_packed_prefill():
     tables = [[f + j if j < c else -1 for j in range(width)] for f, c in zip(first, ctx)]
     ref = O.default().decode(hq[rows].contiguous(), kc, vc, tables, ctx, scale_of(d))
     assert_close(out[rows], ref, "packed_prefill sampled rows")
+
+
+def _scale_rows(t, rows, factor):
+    """Multiply bf16 rows in place (result rounded to bf16)."""
+    t[rows] = (t[rows].float() * factor).to(torch.bfloat16)
+
+
+def test_prefill_v_beyond_fp16_range():
+    """V anywhere in bf16's range: sequence 0's V is scaled by 2^15 (values up
+    to about 1.3e5, beyond fp16's largest, 65504), sequence 1's by 2^-20
+    (below 2^-14: fp16 subnormals), sequence 2 keeps N(0, 1).  Paged and
+    packed.  Attention is linear in V, so a sequence whose V is scaled by F is
+    held to the bar at its own scale: out / F against the oracle's / F (F a
+    power of two: the division is exact and keeps bf16 values bf16)."""
+    log("prefill with V beyond fp16's range and below its normal range")
+    bs = 16
+    specs = [(40, 70), (17, 33), (64, 50)]
+    plan = custom_plan(specs, bs, 8, 2, 128, seed=21, extra_blocks=2, kind="prefill")
+    tens = make_tensors(plan, DEV, poison=True)
+    D = plan.H_kv * plan.d
+    factors = [2.0 ** 15, 2.0 ** -20, 1.0]
+    meta = pkv.prepare_metadata(plan.seqs, bs, plan.max_blocks_per_seq)
+    row0 = 0
+    for s, f in zip(plan.seqs, factors):
+        blocks = torch.tensor(s.block_ids, dtype=torch.long, device=DEV)
+        vc = tens.pool[1, 0]
+        vc[blocks] = (vc[blocks].float() * f).to(torch.bfloat16)
+        _scale_rows(tens.kv_new[0, :, D:], slice(row0, row0 + s.num_new), f)
+        row0 += s.num_new
+    vmax = tens.pool[1, 0].float().nan_to_num(0).abs().max().item()
+    assert vmax > 65504, vmax  # some V values really are beyond fp16's range
+    host = cpu_copy(tens)
+    dm = device_meta(meta, DEV)
+    gpu_store(plan, tens, dm)
+    out = gpu_attention(plan, tens, dm)
+    torch.cuda.synchronize()
+    ometa = oracle_meta(plan)
+    oracle_store(host, ometa)
+    ref = oracle_attention(plan, host, ometa)
+    cq = ometa["cu_seqlens_q"]
+
+    def check(o, r, what):
+        for b, f in enumerate(factors):
+            rows = slice(cq[b], cq[b + 1])
+            got = o[rows].detach().float().cpu().double()
+            assert_close(got / f, r[rows] / f, f"{what}, V scaled by 2^{round(math.log2(f))} "
+                                               f"(sequence {b}), judged at that scale")
+
+    check(out, ref, "paged prefill")
+
+    # the packed form over the same rows: keys of each sequence gathered in order
+    ks, vs, cu_k = [], [], [0]
+    for s in plan.seqs:
+        rows = torch.tensor([s.block_ids[j // bs] * bs + j % bs for j in range(s.total)],
+                            dtype=torch.long)
+        ks.append(host.k_cache().reshape(-1, plan.H_kv, plan.d)[rows])
+        vs.append(host.v_cache().reshape(-1, plan.H_kv, plan.d)[rows])
+        cu_k.append(cu_k[-1] + s.total)
+    k, v = torch.cat(ks), torch.cat(vs)
+    cq_t = torch.tensor(cq, dtype=torch.int32, device=DEV)
+    ck_t = torch.tensor(cu_k, dtype=torch.int32, device=DEV)
+    outp = pkv.prefill_varlen_packed(tens.q[0], k.to(DEV), v.to(DEV), cq_t, ck_t,
+                                     max(s.num_new for s in plan.seqs),
+                                     max(s.total for s in plan.seqs), scale_of(plan.d))
+    torch.cuda.synchronize()
+    refp = O.default().prefill_packed(host.q[0], k, v, cq, cu_k, scale_of(plan.d))
+    check(outp, refp, "packed prefill")
