@@ -45,19 +45,17 @@ int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t
 
 /*
  * Plain streaming read of `bytes` bytes (a multiple of 16, 16-byte aligned
- * src) with 16-byte loads, xor-folded as above.  grid_blocks workgroups of
- * 256 lanes stride over the buffer (0 picks 8 per compute unit).
+ * src) with 16-byte loads, xor-folded as above: one workgroup of 256 lanes
+ * per contiguous 256 KiB chunk, eight loads per lane in flight.
  */
-int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid_blocks,
-                   hipStream_t stream);
+int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
  * Plain device copy of `bytes` bytes (a multiple of 16; both pointers 16-byte
- * aligned) with 16-byte loads and stores: the known-size kernel that scales
- * the FETCH_SIZE / WRITE_SIZE counters, and a copy ceiling.
+ * aligned) with 16-byte loads and stores, chunked as the read: the known-size
+ * kernel that scales the FETCH_SIZE / WRITE_SIZE counters, and a copy ceiling.
  */
-int pkv_probe_copy(void* dst, const void* src, int64_t bytes, int32_t grid_blocks,
-                   hipStream_t stream);
+int pkv_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
 /*
  * Dense bf16 MFMA issue rate: every wavefront runs `iters` rounds of

@@ -62,32 +62,41 @@ __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restri
   if (acc == kNever) sink[0] = acc;
 }
 
-// Grid-stride read, four 16-byte loads per lane per round.
+// Each workgroup streams one contiguous 256 KiB chunk (the last one may be
+// shorter), eight 16-byte loads per lane in flight: the fastest of the plain
+// patterns measured on this device (grid-stride loops ran 3-10% slower).
+constexpr int64_t kChunk16 = (256 << 10) / 16;  // 16-byte units per chunk
+
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                    uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kChunk16;
+  const int64_t end = min(base + kChunk16, n16);
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+  int64_t i = base + threadIdx.x;
+  for (; i + 7 * 256 < end; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + k * 256];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= fold(v[k]);
   }
-  for (; i < n16; i += stride) acc ^= fold(src[i]);
+  for (; i < end; i += 256) acc ^= fold(src[i]);
   if (acc == kNever) sink[0] = acc;
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(u32x4* __restrict__ dst,
                                                    const u32x4* __restrict__ src, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    dst[i] = a;
-    dst[i + stride] = b;
-    dst[i + 2 * stride] = c;
-    dst[i + 3 * stride] = d;
+  const int64_t base = (int64_t)blockIdx.x * kChunk16;
+  const int64_t end = min(base + kChunk16, n16);
+  int64_t i = base + threadIdx.x;
+  for (; i + 7 * 256 < end; i += 8 * 256) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + k * 256];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[i + k * 256] = v[k];
   }
-  for (; i < n16; i += stride) dst[i] = src[i];
+  for (; i < end; i += 256) dst[i] = src[i];
 }
 
 // CH independent accumulator chains of 32x32x16 MFMAs on register operands.
@@ -127,14 +136,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : 3; }
 
-int default_grid(int32_t grid_blocks) {
-  if (grid_blocks > 0) return grid_blocks;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  return 8 * cus;
-}
-
 template <int CH>
 void launch_mfma(dim3 grid, float* sink, int32_t iters, bool f16, hipStream_t stream) {
   if (f16)
@@ -168,20 +169,20 @@ int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t
   return status(hipGetLastError());
 }
 
-int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid_blocks,
-                   hipStream_t stream) {
-  if (!src || !sink || bytes < 16 || bytes % 16 || !aligned16(src) || grid_blocks < 0) return 1;
-  hipLaunchKernelGGL(read_kernel, dim3(default_grid(grid_blocks)), dim3(256), 0, stream,
+int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 || !aligned16(src)) return 1;
+  const int64_t chunks = (bytes / 16 + kChunk16 - 1) / kChunk16;
+  if (chunks > INT32_MAX) return 1;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)chunks), dim3(256), 0, stream,
                      static_cast<const u32x4*>(src), bytes / 16, sink);
   return status(hipGetLastError());
 }
 
-int pkv_probe_copy(void* dst, const void* src, int64_t bytes, int32_t grid_blocks,
-                   hipStream_t stream) {
-  if (!src || !dst || bytes < 16 || bytes % 16 || !aligned16(src) || !aligned16(dst) ||
-      grid_blocks < 0)
-    return 1;
-  hipLaunchKernelGGL(copy_kernel, dim3(default_grid(grid_blocks)), dim3(256), 0, stream,
+int pkv_probe_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst || bytes < 16 || bytes % 16 || !aligned16(src) || !aligned16(dst)) return 1;
+  const int64_t chunks = (bytes / 16 + kChunk16 - 1) / kChunk16;
+  if (chunks > INT32_MAX) return 1;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)chunks), dim3(256), 0, stream,
                      static_cast<u32x4*>(dst), static_cast<const u32x4*>(src), bytes / 16);
   return status(hipGetLastError());
 }

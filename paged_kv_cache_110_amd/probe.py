@@ -27,8 +27,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.pkv_probe_paged_read.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, P]
-    lib.pkv_probe_read.argtypes = [P, I64, P, I32, P]
-    lib.pkv_probe_copy.argtypes = [P, P, I64, I32, P]
+    lib.pkv_probe_read.argtypes = [P, I64, P, P]
+    lib.pkv_probe_copy.argtypes = [P, P, I64, P]
     lib.pkv_probe_mfma.argtypes = [P, I32, I32, I32, I32, I32, P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_int
@@ -63,15 +63,15 @@ def paged_read(k_cache, v_cache, pages: torch.Tensor, sink: torch.Tensor) -> Non
         sink.data_ptr(), _stream()))
 
 
-def read(src: torch.Tensor, sink: torch.Tensor, grid_blocks: int = 0) -> None:
+def read(src: torch.Tensor, sink: torch.Tensor) -> None:
     _check("pkv_probe_read", load().pkv_probe_read(
-        src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), grid_blocks, _stream()))
+        src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), _stream()))
 
 
-def copy(dst: torch.Tensor, src: torch.Tensor, grid_blocks: int = 0) -> None:
+def copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     assert dst.numel() * dst.element_size() == src.numel() * src.element_size()
     _check("pkv_probe_copy", load().pkv_probe_copy(
-        dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), grid_blocks, _stream()))
+        dst.data_ptr(), src.data_ptr(), src.numel() * src.element_size(), _stream()))
 
 
 def mfma(sink: torch.Tensor, num_cus: int, waves_per_simd: int, iters: int, chains: int,

@@ -357,10 +357,10 @@ def test_probe_library_exports_and_argument_checks():
     assert lib.pkv_probe_paged_read(p, p, p, 0, 4, 8, 128, 256, p, None) == 1
     assert lib.pkv_probe_paged_read(p + 2, p, p, 1, 4, 8, 128, 256, p, None) == 1
     # read / copy: sizes that are not whole 16-byte chunks, misaligned buffers
-    assert lib.pkv_probe_read(p, 24, p, 0, None) == 1
-    assert lib.pkv_probe_read(p + 8, 32, p, 0, None) == 1
-    assert lib.pkv_probe_copy(p, p, 0, 0, None) == 1
-    assert lib.pkv_probe_copy(p + 4, p, 32, 0, None) == 1
+    assert lib.pkv_probe_read(p, 24, p, None) == 1
+    assert lib.pkv_probe_read(p + 8, 32, p, None) == 1
+    assert lib.pkv_probe_copy(p, p, 0, None) == 1
+    assert lib.pkv_probe_copy(p + 4, p, 32, None) == 1
     # mfma: chain counts and occupancies outside the supported set
     assert lib.pkv_probe_mfma(p, 256, 2, 10, 3, 0, None) == 1
     assert lib.pkv_probe_mfma(p, 256, 9, 10, 4, 0, None) == 1
