@@ -47,6 +47,7 @@
 //    bf16.  A segment cut by share boundaries writes an fp32 partial
 //    (m, l, acc[d]) per piece into its share's partial slots, and
 //    decode_merge_kernel combines the pieces in share order.
+#include <limits.h>
 #include <stdlib.h>
 
 #include <type_traits>
@@ -750,18 +751,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int sub = lane % 8;  // d chunk
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // b * H_q + h
   if (row >= (int64_t)B * H_q) return;
-  const int b = (int)(row / H_q);
+  // row / H_q in 32 bits when every row index fits (a uniform branch)
+  const int b = (int64_t)B * H_q <= INT32_MAX ? (int)((uint32_t)row / (uint32_t)H_q)
+                                              : (int)(row / H_q);
   const int hq = (int)(row - (int64_t)b * H_q);
   uint16_t* op = out + row * D + sub * EPL;
-  if (context_lens[b] <= 0) {
+  // the length and the segment record are independent: both loads in flight
+  const int H_kv = H_q / G;
+  const int32_t len = context_lens[b];
+  const SegInfo info = ws_seg[(int64_t)b * H_kv + hq / G];
+  // used here, so the compiler cannot sink the record's load below the branch
+  asm volatile("" ::"v"(info.k_first), "v"(info.k_last));
+  if (len <= 0) {
     if (pg == 0) {
 #pragma unroll
       for (int w = 0; w < EPL / 8; ++w) st16(op + 8 * w, u32x4{0u, 0u, 0u, 0u});
     }
     return;
   }
-  const int H_kv = H_q / G;
-  const SegInfo info = ws_seg[(int64_t)b * H_kv + hq / G];
   if (info.k_last <= info.k_first) return;  // one piece: written by the decode kernel
   if (info.k_first < 0 || info.k_last >= max_shares) return;  // not from this call's layout
   const int nparts = info.k_last - info.k_first + 1;
