@@ -107,6 +107,28 @@ def spread(ms_list) -> dict:
                 n=len(ms_list))
 
 
+# Secondary workloads warm up for at least this much wall time (besides their
+# step count): the device's clocks drop while it idles (during the oracle legs,
+# for one) and need some tens of ms of load to come back, so a warm-up of a few
+# sub-millisecond calls leaves the first timed calls about 10% slow.
+SECONDARY_WARM_S = 0.25
+
+
+def warm(torch, fn, calls, seconds=0.0):
+    """At least `calls` untimed calls fn(i), and more until `seconds` of wall
+    time have passed (synchronising every 8 calls past the minimum, so the wall
+    time follows the device's); returns how many ran."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < calls or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i >= calls and i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
 def timed_calls(torch, fn, n):
     """n calls fn(i), each between its own pair of HIP events on the current
     stream; returns the per-call durations (ms)."""
@@ -291,9 +313,10 @@ def oracle_prefill_leg(plan, tens, outs, budget_s, log, tail: int = 64) -> dict:
 
 # ------------------------------------------------------------ attention workloads
 
-def run_workload(name, steps, warmup, pools, torch, pkv, probe, log, cpu_budget=None):
+def run_workload(name, steps, warmup, pools, torch, pkv, probe, log, cpu_budget=None, warm_s=0.0):
     """Timed steps of one named workload, the probe ceiling over the same
-    pages (decode), and the oracle leg (cpu_budget seconds, None = skipped)."""
+    pages (decode), and the oracle leg (cpu_budget seconds, None = skipped).
+    Warm-up: `warmup` steps, continued until `warm_s` seconds have passed."""
     from workloads import make_plan, make_tensors
 
     plan = make_plan(name)
@@ -331,11 +354,12 @@ def run_workload(name, steps, warmup, pools, torch, pkv, probe, log, cpu_budget=
                                dm["cu_seqlens_k"], dm["max_seqlen_q"], dm["max_seqlen_k"], scale,
                                out=out)
 
-    for i in range(warmup):
+    def step(i):
         for layer in range(L):
             store(i, layer)
             attention(i, layer)
-    torch.cuda.synchronize()
+
+    warm_steps = warm(torch, step, warmup, warm_s)
     # the timed region: whole steps; a pair of HIP events around every attention call
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps * L)]
@@ -351,7 +375,7 @@ def run_workload(name, steps, warmup, pools, torch, pkv, probe, log, cpu_budget=
     wall = time.perf_counter() - start
     call_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / steps
-    res = dict(plan=plan, ms_per_step=ms_step, call=spread(call_ms))
+    res = dict(plan=plan, ms_per_step=ms_step, call=spread(call_ms), warmup_steps=warm_steps)
     if plan.kind == "decode":
         views = [(t.k_cache(l), t.v_cache(l)) for l in range(L) for t in tens]
         res["read_ceiling"] = paged_read_ceiling(torch, probe, plan, meta, views)
@@ -371,7 +395,7 @@ def summarize(res, ceilings) -> dict:
     call = res["call"]
     med_s = call["median"] * 1e-3
     out = dict(workload=plan.name, layers=plan.layers, ms_per_step=round(res["ms_per_step"], 4),
-               attn_call_ms=call)
+               attn_call_ms=call, warmup_steps=res["warmup_steps"])
     if plan.kind == "decode":
         per_call = decode_bytes(plan)
         per_step = (per_call + store_bytes(plan)) * plan.layers
@@ -425,9 +449,8 @@ def run_packed(steps, warmup, torch, pkv, log, ceilings):
     out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     scale = 1.0 / math.sqrt(cfg["d"])
     mx = max(lens)
-    for _ in range(warmup):
-        pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out)
-    torch.cuda.synchronize()
+    warm(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale, out=out),
+         warmup, SECONDARY_WARM_S)
     ms = timed_calls(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale,
                                                                 out=out), steps)
     med = statistics.median(ms)
@@ -482,9 +505,7 @@ def run_graph(steps, warmup, torch, pkv, log):
                 pkv.decode(tens.q[l][:batch], kc, vc, bt, cl, scale, out=outs[l], workspace=ws)
 
         def timed(fn):
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
+            warm(torch, lambda i: fn(), warmup, SECONDARY_WARM_S)
             t0 = time.perf_counter()
             for _ in range(steps):
                 fn()
@@ -535,9 +556,7 @@ def run_meta(steps, warmup, torch, pkv, log):
             pkv.prepare_metadata_device(None, computed, sched, table, bs, maxb, total, out=bufs)
 
         def wall(fn):
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
+            warm(torch, lambda i: fn(), warmup, SECONDARY_WARM_S)
             t0 = time.perf_counter()
             for _ in range(steps):
                 fn()
@@ -563,9 +582,8 @@ def run_sample(steps, warmup, torch, pkv, log):
     out = torch.empty(cfg["B"], dtype=torch.int64, device="cuda")
     ws = torch.empty(pkv.sample_workspace_size(cfg["B"], cfg["V"]), dtype=torch.uint8, device="cuda")
     step_offsets = [offsets + i for i in range(steps)]  # a fresh draw per step
-    for _ in range(warmup):
-        pkv.sample_gumbel(logits, seeds, temps, offsets, out=out, workspace=ws)
-    torch.cuda.synchronize()
+    warm(torch, lambda i: pkv.sample_gumbel(logits, seeds, temps, offsets, out=out, workspace=ws),
+         warmup, SECONDARY_WARM_S)
     calls = timed_calls(torch, lambda i: pkv.sample_gumbel(logits, seeds, temps, step_offsets[i],
                                                            out=out, workspace=ws), steps)
     ms = statistics.median(calls)
@@ -651,7 +669,8 @@ def main() -> int:
     for name in ATTENTION:
         if name == args.workload or name not in wanted:
             continue
-        r = run_workload(name, n2, 2, pools_of(name), torch, pkv, probe, log, cpu_budget=cpu2)
+        r = run_workload(name, n2, 2, pools_of(name), torch, pkv, probe, log, cpu_budget=cpu2,
+                         warm_s=SECONDARY_WARM_S)
         secondary[name] = summarize(r, ceilings)
         log(json.dumps(secondary[name]))
     if "packed_prefill" in wanted:
