@@ -301,18 +301,32 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void prefill_kernel(
 
   // One 64-key tile in three parts: S^T = K Q^T (MFMA), the online softmax
   // (VALU; produces P in fp16), O^T += V^T P^T (MFMA).
+  // The two 32-key halves are independent chains, interleaved.  The K reads
+  // run up to four pairs ahead of their MFMAs (an LDS read takes longer than
+  // the two MFMAs between a pair and the next): the first reads, then two
+  // MFMAs and two reads at a time, then the remaining MFMAs.  Left to itself,
+  // the compiler (at 254 registers) issued each read just one MFMA ahead.
   auto score_mfma = [&](const uint16_t* kt_lds, f32x16 (&sacc)[2]) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int kb = 0; kb < 2; ++kb) {
         const u32x4 a =
             *reinterpret_cast<const u32x4*>(kt_lds + (kbase_lane ^ (16 * ks)) + kb * 32 * D);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks],
                                                            sacc[kb], 0, 0, 0);
       }
+    constexpr int kReads = 2 * KS;                       // one per MFMA
+    constexpr int kAhead = kReads < 8 ? kReads : 8;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
+#pragma unroll
+    for (int g = 0; g < (kReads - kAhead) / 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x8, 2, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x8, kAhead, 0);
   };
   // Mask, running max and rescale of one tile's scores.  The fast pass
   // rescales lazily (P up to 2^8); the exact pass whenever the maximum grows
