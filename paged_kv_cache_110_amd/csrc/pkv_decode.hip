@@ -369,8 +369,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       const int off = (r <= last ? r : last) * rs;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        kx[i][w] = ld16(kt + off + dofs(w));
-        vx[i][w] = ld16(vt + off + dofs(w));
+        kx[i][w] = ld16_stream(kt + off + dofs(w));
+        vx[i][w] = ld16_stream(vt + off + dofs(w));
       }
     }
     if (real && !switch_pending) step_unit(L);
