@@ -145,10 +145,11 @@ def timed_calls(torch, fn, n):
 # ----------------------------------------------------------------- ceilings
 
 def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dict:
-    """What the device sustains with hand-written probe kernels: a plain
-    streaming read and a plain copy of a buffer of known size, and the dense
-    MFMA issue rate (bf16 and fp16 32x32x16, register operands) at the best of
-    a few occupancies."""
+    """What the device sustains with hand-written probe kernels: a streaming
+    read of a buffer of known size with plain loads and with non-temporal ones
+    (the form the decode's K/V loads take), a plain copy, and the dense MFMA
+    issue rate (bf16 and fp16 32x32x16, register operands) at the best of a
+    few occupancies."""
     n = int(gib * (1 << 30))
     src = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda").normal_()
     dst = torch.empty_like(src)
@@ -156,11 +157,15 @@ def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dic
     res = {}
     for _ in range(2):
         probe.read(src, sink)
+        probe.read(src, sink, nontemporal=True)
         probe.copy(dst, src)
     rd = timed_calls(torch, lambda i: probe.read(src, sink), runs)
+    rdn = timed_calls(torch, lambda i: probe.read(src, sink, nontemporal=True), runs)
     cp = timed_calls(torch, lambda i: probe.copy(dst, src), runs)
-    res["read"] = dict(kernel="read_kernel (libpkv_probe)", bytes=n, ms=spread(rd),
+    res["read"] = dict(kernel="read_kernel<plain loads> (libpkv_probe)", bytes=n, ms=spread(rd),
                        gb_per_s=round(n / statistics.median(rd) / 1e6, 1))
+    res["read_nt"] = dict(kernel="read_kernel<non-temporal loads> (libpkv_probe)", bytes=n,
+                          ms=spread(rdn), gb_per_s=round(n / statistics.median(rdn) / 1e6, 1))
     res["copy"] = dict(kernel="copy_kernel (libpkv_probe)", bytes=2 * n, ms=spread(cp),
                        gb_per_s=round(2 * n / statistics.median(cp) / 1e6, 1))
     del src, dst
@@ -180,15 +185,17 @@ def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dic
                             tflops=round(tf, 1), waves_per_simd=waves, chains=chains,
                             flops=flops, ms=spread(ms))
         res[name] = best
-    log(f"ceilings: read {res['read']['gb_per_s']} GB/s, copy {res['copy']['gb_per_s']} GB/s, "
+    log(f"ceilings: read {res['read']['gb_per_s']} GB/s (non-temporal {res['read_nt']['gb_per_s']}), "
+        f"copy {res['copy']['gb_per_s']} GB/s, "
         f"bf16 MFMA {res['mfma_bf16']['tflops']} TFLOP/s, f16 MFMA {res['mfma_f16']['tflops']} TFLOP/s")
     return res
 
 
 def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20) -> dict:
     """The load-only probe over the same pages as the decode (same tables and
-    lengths), rotating over the given (k_cache, v_cache) views so consecutive
-    runs do not find their bytes in the last-level cache."""
+    lengths, the same non-temporal loads), rotating over the given (k_cache,
+    v_cache) views so consecutive runs do not find their bytes in the
+    last-level cache."""
     from paged_kv_cache_110_amd.probe import pages_of
 
     pages = pages_of(meta["block_tables"], meta["context_lens"], plan.block_size).to("cuda")
@@ -196,13 +203,13 @@ def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20) -> dict:
 
     def run(i):
         kc, vc = views[i % len(views)]
-        probe.paged_read(kc, vc, pages, sink)
+        probe.paged_read(kc, vc, pages, sink, nontemporal=True)
 
     for i in range(2):
         run(i)
     ms = timed_calls(torch, run, runs)
     nbytes = kv_bytes(plan)
-    return dict(kernel="paged_read_kernel (libpkv_probe)", bytes=nbytes, ms=spread(ms),
+    return dict(kernel="paged_read_kernel<non-temporal loads> (libpkv_probe)", bytes=nbytes, ms=spread(ms),
                 gb_per_s=round(nbytes / statistics.median(ms) / 1e6, 1),
                 pages=int(pages.shape[0]))
 
@@ -688,7 +695,8 @@ def main() -> int:
         value, unit = s["gb_per_s"], "GB/s"
         roofline.update(
             avg_launch_ms=s["attn_call_ms"]["mean"], launch_ms=s["attn_call_ms"],
-            copy_ceiling=ceilings["copy"]["gb_per_s"], plain_read_ceiling=ceilings["read"]["gb_per_s"])
+            copy_ceiling=ceilings["copy"]["gb_per_s"], plain_read_ceiling=ceilings["read"]["gb_per_s"],
+            nontemporal_read_ceiling=ceilings["read_nt"]["gb_per_s"])
     else:
         value, unit = s["roofline"]["achieved"], "TFLOP/s"
         roofline.update(traffic=None, avg_launch_ms=s["attn_call_ms"]["mean"],

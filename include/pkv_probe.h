@@ -35,20 +35,25 @@ extern "C" {
  *                     [0, num_blocks) reads nothing; token counts are clamped
  *                     to block_size
  *   sink              one uint32
+ *   nontemporal       nonzero: the loads carry the non-temporal hint, as the
+ *                     decode's K/V loads do
  * One workgroup of 64 lanes per (page, head).
  * PKV_EINVAL: null pointers, num_pages < 1, num_blocks < 1, H_kv < 1, d not
  * 64 or 128, block_size not a power of two >= 16, misaligned caches.
  */
 int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t* pages,
                          int32_t num_pages, int32_t num_blocks, int32_t H_kv, int32_t d,
-                         int32_t block_size, uint32_t* sink, hipStream_t stream);
+                         int32_t block_size, uint32_t* sink, int32_t nontemporal,
+                         hipStream_t stream);
 
 /*
  * Plain streaming read of `bytes` bytes (a multiple of 16, 16-byte aligned
  * src) with 16-byte loads, xor-folded as above: one workgroup of 256 lanes
- * per contiguous 256 KiB chunk, eight loads per lane in flight.
+ * per contiguous 256 KiB chunk, eight loads per lane in flight; with the
+ * non-temporal hint when `nontemporal` is nonzero.
  */
-int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, int32_t nontemporal,
+                   hipStream_t stream);
 
 /*
  * Plain device copy of `bytes` bytes (a multiple of 16; both pointers 16-byte

@@ -1,6 +1,8 @@
 // Measurement probes (include/pkv_probe.h): a load-only pass over the decode's
 // paged K/V rows, a plain streaming read and copy, and a register-only MFMA
-// loop.  Built into libpkv_probe.so, apart from the attention library.
+// loop.  Built into libpkv_probe.so, apart from the attention library.  The
+// two reads take the load instruction's non-temporal hint as an option (the
+// decode streams its K/V with it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -12,6 +14,7 @@ namespace {
 using pkv::bf16x8;
 using pkv::f32x16;
 using pkv::ld16;
+using pkv::ld16_stream;
 using pkv::u32x4;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -20,10 +23,16 @@ constexpr uint32_t kNever = 0x9e3779b9u;  // the fold practically never equals i
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
 
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  if constexpr (NT) return ld16_stream(p);
+  else return ld16(p);
+}
+
 // One wavefront per (page, KV head): the page's used rows of that head, K and
 // V, two 16-token tiles per round.  A row of one head is d bf16 = d/8 lanes of
 // 16 bytes, so one load instruction covers 64 / (d/8) rows.
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restrict__ k_cache,
                                                         const uint16_t* __restrict__ v_cache,
                                                         const int32_t* __restrict__ pages,
@@ -51,14 +60,14 @@ __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 2 * kLoadsPerTile; ++i) {
       const int tok = t + i * kRowsPerLoad + r0;
-      kr[i] = ld16(kb + tok * row);
-      vr[i] = ld16(vb + tok * row);
+      kr[i] = load16<NT>(kb + tok * row);
+      vr[i] = load16<NT>(vb + tok * row);
     }
 #pragma unroll
     for (int i = 0; i < 2 * kLoadsPerTile; ++i) acc ^= fold(kr[i]) ^ fold(vr[i]);
   }
   for (int tok = t + r0; tok < used; tok += kRowsPerLoad)  // the page's last rows
-    acc ^= fold(ld16(kb + tok * row)) ^ fold(ld16(vb + tok * row));
+    acc ^= fold(load16<NT>(kb + tok * row)) ^ fold(load16<NT>(vb + tok * row));
   if (acc == kNever) sink[0] = acc;
 }
 
@@ -67,6 +76,7 @@ __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restri
 // patterns measured on this device (grid-stride loops ran 3-10% slower).
 constexpr int64_t kChunk16 = (256 << 10) / 16;  // 16-byte units per chunk
 
+template <bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                    uint32_t* __restrict__ sink) {
   const int64_t base = (int64_t)blockIdx.x * kChunk16;
@@ -76,11 +86,11 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   for (; i + 7 * 256 < end; i += 8 * 256) {
     u32x4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[i + k * 256];
+    for (int k = 0; k < 8; ++k) v[k] = load16<NT>(&src[i + k * 256]);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc ^= fold(v[k]);
   }
-  for (; i < end; i += 256) acc ^= fold(src[i]);
+  for (; i < end; i += 256) acc ^= fold(load16<NT>(&src[i]));
   if (acc == kNever) sink[0] = acc;
 }
 
@@ -150,7 +160,8 @@ extern "C" {
 
 int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t* pages,
                          int32_t num_pages, int32_t num_blocks, int32_t H_kv, int32_t d,
-                         int32_t block_size, uint32_t* sink, hipStream_t stream) {
+                         int32_t block_size, uint32_t* sink, int32_t nontemporal,
+                         hipStream_t stream) {
   if (!k_cache || !v_cache || !pages || !sink || num_pages < 1 || num_blocks < 1 || H_kv < 1)
     return 1;
   if (d != 64 && d != 128) return 1;
@@ -160,21 +171,33 @@ int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t
   const dim3 grid((unsigned)(num_pages * H_kv));
   const auto* kc = static_cast<const uint16_t*>(k_cache);
   const auto* vc = static_cast<const uint16_t*>(v_cache);
-  if (d == 128)
-    hipLaunchKernelGGL(paged_read_kernel<128>, grid, dim3(64), 0, stream, kc, vc, pages,
+  const bool nt = nontemporal != 0;
+  if (d == 128 && nt)
+    hipLaunchKernelGGL((paged_read_kernel<128, true>), grid, dim3(64), 0, stream, kc, vc, pages,
+                       num_blocks, H_kv, block_size, sink);
+  else if (d == 128)
+    hipLaunchKernelGGL((paged_read_kernel<128, false>), grid, dim3(64), 0, stream, kc, vc, pages,
+                       num_blocks, H_kv, block_size, sink);
+  else if (nt)
+    hipLaunchKernelGGL((paged_read_kernel<64, true>), grid, dim3(64), 0, stream, kc, vc, pages,
                        num_blocks, H_kv, block_size, sink);
   else
-    hipLaunchKernelGGL(paged_read_kernel<64>, grid, dim3(64), 0, stream, kc, vc, pages,
+    hipLaunchKernelGGL((paged_read_kernel<64, false>), grid, dim3(64), 0, stream, kc, vc, pages,
                        num_blocks, H_kv, block_size, sink);
   return status(hipGetLastError());
 }
 
-int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+int pkv_probe_read(const void* src, int64_t bytes, uint32_t* sink, int32_t nontemporal,
+                   hipStream_t stream) {
   if (!src || !sink || bytes < 16 || bytes % 16 || !aligned16(src)) return 1;
   const int64_t chunks = (bytes / 16 + kChunk16 - 1) / kChunk16;
   if (chunks > INT32_MAX) return 1;
-  hipLaunchKernelGGL(read_kernel, dim3((unsigned)chunks), dim3(256), 0, stream,
-                     static_cast<const u32x4*>(src), bytes / 16, sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(read_kernel<true>, dim3((unsigned)chunks), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(read_kernel<false>, dim3((unsigned)chunks), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
   return status(hipGetLastError());
 }
 

@@ -26,8 +26,8 @@ def load() -> ctypes.CDLL:
                           "`python -m paged_kv_cache_110_amd.build` (hipcc, gfx950)")
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    lib.pkv_probe_paged_read.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, P]
-    lib.pkv_probe_read.argtypes = [P, I64, P, P]
+    lib.pkv_probe_paged_read.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, I32, P]
+    lib.pkv_probe_read.argtypes = [P, I64, P, I32, P]
     lib.pkv_probe_copy.argtypes = [P, P, I64, P]
     lib.pkv_probe_mfma.argtypes = [P, I32, I32, I32, I32, I32, P]
     for name in EXPORTS:
@@ -56,16 +56,18 @@ def pages_of(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size:
     return torch.tensor(out, dtype=torch.int32).reshape(-1, 2)
 
 
-def paged_read(k_cache, v_cache, pages: torch.Tensor, sink: torch.Tensor) -> None:
+def paged_read(k_cache, v_cache, pages: torch.Tensor, sink: torch.Tensor,
+               nontemporal: bool = True) -> None:
     nb, bs, H_kv, d = k_cache.shape
     _check("pkv_probe_paged_read", load().pkv_probe_paged_read(
         k_cache.data_ptr(), v_cache.data_ptr(), pages.data_ptr(), pages.shape[0], nb, H_kv, d, bs,
-        sink.data_ptr(), _stream()))
+        sink.data_ptr(), int(nontemporal), _stream()))
 
 
-def read(src: torch.Tensor, sink: torch.Tensor) -> None:
+def read(src: torch.Tensor, sink: torch.Tensor, nontemporal: bool = False) -> None:
     _check("pkv_probe_read", load().pkv_probe_read(
-        src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), _stream()))
+        src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), int(nontemporal),
+        _stream()))
 
 
 def copy(dst: torch.Tensor, src: torch.Tensor) -> None:
