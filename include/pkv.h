@@ -148,9 +148,11 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d
  *                 After a PKV_ELAUNCH it must be zero-filled again.
  * The causal mask of the pages' call is a no-op for one query per sequence.
  * The work (every 16-token tile of every (sequence, KV head)) is cut into
- * shares: one static share per resident wavefront of the device (about three
- * quarters of the work), then shrinking shares that wavefronts take from an
- * atomic counter as they finish, so all of them stop at nearly the same time.
+ * shares: one static share per resident wavefront of the device (all of the
+ * work for calls of up to 64 tiles per wavefront, else 3/5 of it up to 128
+ * tiles per wavefront and 2/5 above), then shrinking shares that wavefronts
+ * take from an atomic counter as they finish, so all of them stop at nearly
+ * the same time.  K and V are read with non-temporal loads (each byte once).
  * Pieces of a sequence that span shares are merged with a log-sum-exp rescale
  * in a second kernel, in share order, so the result does not depend on which
  * wavefront took which share: results are deterministic run to run on one
