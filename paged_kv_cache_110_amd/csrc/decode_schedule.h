@@ -9,9 +9,10 @@
 // segments are not cut into more pieces than the merge gathers quickly.
 // Larger calls:
 // Level 0: one static share of S0 units per wavefront, ending at unit P1:
-// about 60% of the work for calls of at most kMidStaticUnits units per
-// wavefront, 40% for larger ones (a small call loses more to share changes
-// and split pieces, a large one more to wavefronts drifting apart).  Levels 1..kLevels-2 hold N = ceil(W / 2) shares
+// for calls of at most kMidStaticUnits units per wavefront 70% of the work
+// (80% for the decode's MFMA form, whose wavefronts run at more even rates),
+// 40% for larger ones (a small call loses more to share changes and split
+// pieces, a large one more to wavefronts drifting apart).  Levels 1..kLevels-2 hold N = ceil(W / 2) shares
 // each and are handed out in order through an atomic counter: level 1's
 // shares hold S1 units (what is left, spread over 2W), each further level
 // three quarters as many (at least kDynMinUnits).  The last level has W
@@ -39,8 +40,12 @@ struct ShareSchedule {
 #define PKV_SCHED_STATIC_DEN 5
 #endif
 #ifndef PKV_SCHED_MID_STATIC_NUM
-#define PKV_SCHED_MID_STATIC_NUM 3  // static part of calls up to kMidStaticUnits per wavefront: 3/5
-#define PKV_SCHED_MID_STATIC_DEN 5
+#define PKV_SCHED_MID_STATIC_NUM 7  // static part of calls up to kMidStaticUnits per wavefront: 7/10
+#define PKV_SCHED_MID_STATIC_DEN 10
+#endif
+#ifndef PKV_SCHED_MID_STATIC_MF_NUM
+#define PKV_SCHED_MID_STATIC_MF_NUM 4  // the same for the MFMA form: 4/5
+#define PKV_SCHED_MID_STATIC_MF_DEN 5
 #endif
 #ifndef PKV_SCHED_DYN_MIN
 #define PKV_SCHED_DYN_MIN 16
@@ -61,8 +66,8 @@ struct ShareSchedule {
 
   int T, W, S0, P1, S1, N;
 
-  // 0 < W; 0 <= T.
-  static PKV_HD ShareSchedule make(int T, int W) {
+  // 0 < W; 0 <= T.  mfma_form: the schedule of the decode's MFMA form.
+  static PKV_HD ShareSchedule make(int T, int W, bool mfma_form = false) {
     ShareSchedule s;
     s.T = T;
     s.W = W;
@@ -71,8 +76,10 @@ struct ShareSchedule {
       s.S0 = per_wave < PKV_SCHED_SMALL_MIN ? PKV_SCHED_SMALL_MIN : (int)per_wave;
     } else {
       const bool mid = per_wave <= kMidStaticUnits;
-      const int64_t num = mid ? PKV_SCHED_MID_STATIC_NUM : PKV_SCHED_STATIC_NUM;
-      const int64_t den = mid ? PKV_SCHED_MID_STATIC_DEN : PKV_SCHED_STATIC_DEN;
+      const int64_t num = !mid ? PKV_SCHED_STATIC_NUM
+                               : (mfma_form ? PKV_SCHED_MID_STATIC_MF_NUM : PKV_SCHED_MID_STATIC_NUM);
+      const int64_t den = !mid ? PKV_SCHED_STATIC_DEN
+                               : (mfma_form ? PKV_SCHED_MID_STATIC_MF_DEN : PKV_SCHED_MID_STATIC_DEN);
       const int s0 = (int)(((int64_t)T * num / den) / W);
       s.S0 = s0 < kMinStaticUnits ? kMinStaticUnits : s0;
     }

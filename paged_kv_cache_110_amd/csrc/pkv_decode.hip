@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   // Divisions run on the vector ALU: pin every result that addresses memory
   // to scalar registers, so block-table reads stay scalar loads instead of
   // vector loads whose wait would drain the tile ring.
-  ShareSchedule sch = ShareSchedule::make(T, W);
+  ShareSchedule sch = ShareSchedule::make(T, W, MF);
   sch.S0 = uniform(sch.S0);
   sch.P1 = uniform(sch.P1);
   sch.S1 = uniform(sch.S1);

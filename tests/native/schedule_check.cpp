@@ -1,6 +1,7 @@
 // Checks the decode share schedule (paged_kv_cache_110_amd/csrc/decode_schedule.h)
-// on the host.  Reads "T W" pairs from stdin; for each prints "ok T W" or the
-// first violated property and exits non-zero.
+// on the host, for both forms of the decode (VALU and MFMA, whose static
+// fractions differ).  Reads "T W" pairs from stdin; prints the first violated
+// property and exits non-zero, or "ok" and the case count.
 //   1. the non-empty shares, in index order, tile [0, T) contiguously;
 //   2. empty shares only follow the last non-empty one;
 //   3. share_of(u) names the share whose range holds u;
@@ -21,8 +22,8 @@ static int fail(const char* what, long long T, long long W, long long a, long lo
   return 1;
 }
 
-static int check(int T, int W) {
-  const pkv::ShareSchedule s = pkv::ShareSchedule::make(T, W);
+static int check(int T, int W, bool mfma_form) {
+  const pkv::ShareSchedule s = pkv::ShareSchedule::make(T, W, mfma_form);
   const int n = s.num_shares();
   if (n > pkv::ShareSchedule::max_shares(W)) return fail("share count", T, W, n, 0);
   long long next = 0;  // first unit not yet covered
@@ -83,7 +84,7 @@ int main() {
   long long T = 0, W = 0;
   int cases = 0;
   while (std::scanf("%lld %lld", &T, &W) == 2) {
-    if (check((int)T, (int)W)) return 1;
+    if (check((int)T, (int)W, false) || check((int)T, (int)W, true)) return 1;
     ++cases;
   }
   std::printf("ok %d cases\n", cases);
