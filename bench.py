@@ -634,7 +634,7 @@ def main() -> int:
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build measures the "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the benchmark measures the "
               "path on one GPU and has no multi-GPU mode", file=sys.stderr)
         return 2
 

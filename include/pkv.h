@@ -55,7 +55,7 @@ extern "C" {
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_EINVAL = 1,       /* an argument violates a documented constraint */
-  PKV_EUNSUPPORTED = 2, /* valid, but not a shape this build has kernels for */
+  PKV_EUNSUPPORTED = 2, /* valid, but not a shape the library has kernels for */
   PKV_ELAUNCH = 3,      /* the HIP runtime reported an error at launch */
   PKV_ESCRATCH = 4      /* more scratch than pkv_sample_gumbel_noalloc's fixed array holds */
 } pkv_status;
