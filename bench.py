@@ -21,7 +21,8 @@ with its own roofline, call-time spread and oracle timing.
 
 Timing: the timed region (K steps) brackets every attention call with a pair
 of HIP events on the launch stream (torch's current stream, which the library
-uses); median, min and max over those calls are reported, and the wall clock
+uses); mean, median, min and max over those calls are reported, the rooflines
+use the mean (the average launch duration), and the wall clock
 around the whole region gives ms_per_step.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
@@ -163,11 +164,11 @@ def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dic
     rdn = timed_calls(torch, lambda i: probe.read(src, sink, nontemporal=True), runs)
     cp = timed_calls(torch, lambda i: probe.copy(dst, src), runs)
     res["read"] = dict(kernel="read_kernel<plain loads> (libpkv_probe)", bytes=n, ms=spread(rd),
-                       gb_per_s=round(n / statistics.median(rd) / 1e6, 1))
+                       gb_per_s=round(n / statistics.fmean(rd) / 1e6, 1))
     res["read_nt"] = dict(kernel="read_kernel<non-temporal loads> (libpkv_probe)", bytes=n,
-                          ms=spread(rdn), gb_per_s=round(n / statistics.median(rdn) / 1e6, 1))
+                          ms=spread(rdn), gb_per_s=round(n / statistics.fmean(rdn) / 1e6, 1))
     res["copy"] = dict(kernel="copy_kernel (libpkv_probe)", bytes=2 * n, ms=spread(cp),
-                       gb_per_s=round(2 * n / statistics.median(cp) / 1e6, 1))
+                       gb_per_s=round(2 * n / statistics.fmean(cp) / 1e6, 1))
     del src, dst
     torch.cuda.empty_cache()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -179,7 +180,7 @@ def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dic
             probe.mfma(msink, cus, waves, iters, chains, f16)
             ms = timed_calls(torch, lambda i: probe.mfma(msink, cus, waves, iters, chains, f16), 5)
             flops = cus * 4 * waves * iters * chains * 32768
-            tf = flops / (statistics.median(ms) * 1e-3) / 1e12
+            tf = flops / (statistics.fmean(ms) * 1e-3) / 1e12
             if best is None or tf > best["tflops"]:
                 best = dict(kernel=f"mfma_kernel ({'f16' if f16 else 'bf16'} 32x32x16, libpkv_probe)",
                             tflops=round(tf, 1), waves_per_simd=waves, chains=chains,
@@ -210,7 +211,7 @@ def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20) -> dict:
     ms = timed_calls(torch, run, runs)
     nbytes = kv_bytes(plan)
     return dict(kernel="paged_read_kernel<non-temporal loads> (libpkv_probe)", bytes=nbytes, ms=spread(ms),
-                gb_per_s=round(nbytes / statistics.median(ms) / 1e6, 1),
+                gb_per_s=round(nbytes / statistics.fmean(ms) / 1e6, 1),
                 pages=int(pages.shape[0]))
 
 
@@ -400,13 +401,13 @@ def summarize(res, ceilings) -> dict:
     oracle leg."""
     plan = res["plan"]
     call = res["call"]
-    med_s = call["median"] * 1e-3
+    mean_s = call["mean"] * 1e-3  # the average launch duration
     out = dict(workload=plan.name, layers=plan.layers, ms_per_step=round(res["ms_per_step"], 4),
                attn_call_ms=call, warmup_steps=res["warmup_steps"])
     if plan.kind == "decode":
         per_call = decode_bytes(plan)
         per_step = (per_call + store_bytes(plan)) * plan.layers
-        achieved = per_call / med_s / 1e9
+        achieved = per_call / mean_s / 1e9
         rc = res["read_ceiling"]
         out.update(
             gb_per_s=round(per_step / (res["ms_per_step"] * 1e-3) / 1e9, 2),
@@ -427,7 +428,7 @@ def summarize(res, ceilings) -> dict:
                          "decode source changed since")
     else:
         fl = prefill_flops(plan)
-        achieved = fl / med_s / 1e12
+        achieved = fl / mean_s / 1e12
         mc = ceilings["mfma_bf16"]["tflops"] if ceilings else None
         out.update(
             tokens_per_s=round(plan.total_new / (res["ms_per_step"] * 1e-3), 1),
@@ -460,12 +461,12 @@ def run_packed(steps, warmup, torch, pkv, log, ceilings):
          warmup, SECONDARY_WARM_S)
     ms = timed_calls(torch, lambda i: pkv.prefill_varlen_packed(q, k, v, cu, cu, mx, mx, scale,
                                                                 out=out), steps)
-    med = statistics.median(ms)
+    mean = statistics.fmean(ms)
     fl = 4 * cfg["d"] * cfg["H_q"] * sum(causal_pairs(0, n) for n in lens)
-    tf = fl / (med * 1e-3) / 1e12
+    tf = fl / (mean * 1e-3) / 1e12
     mc = ceilings["mfma_bf16"]["tflops"] if ceilings else None
     return dict(workload="packed_prefill", B=cfg["B"], tokens=sum(lens), attn_call_ms=spread(ms),
-                tokens_per_s=round(sum(lens) / (med * 1e-3), 1),
+                tokens_per_s=round(sum(lens) / (mean * 1e-3), 1),
                 roofline=dict(bound="mfma", kernel="prefill_kernel<128,2,4,false>",
                               achieved=round(tf, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                               frac=round(tf / BF16_PEAK_TFLOPS, 4), flops_per_launch=fl,
@@ -593,7 +594,7 @@ def run_sample(steps, warmup, torch, pkv, log):
          warmup, SECONDARY_WARM_S)
     calls = timed_calls(torch, lambda i: pkv.sample_gumbel(logits, seeds, temps, step_offsets[i],
                                                            out=out, workspace=ws), steps)
-    ms = statistics.median(calls)
+    ms = statistics.fmean(calls)
     n = cfg["B"] * cfg["V"]
     nbytes = 2 * n + cfg["B"] * (4 + 8 + 8 + 8)
     res = dict(workload="gumbel_sample", B=cfg["B"], V=cfg["V"], dtype="bf16", bound="alu",
