@@ -192,11 +192,13 @@ def measure_ceilings(torch, probe, log, gib: float = 4.0, runs: int = 10) -> dic
     return res
 
 
-def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20) -> dict:
+def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20,
+                       group_heads: bool = False) -> dict:
     """The load-only probe over the same pages as the decode (same tables and
     lengths, the same non-temporal loads), rotating over the given (k_cache,
     v_cache) views so consecutive runs do not find their bytes in the
-    last-level cache."""
+    last-level cache.  group_heads: the H_kv heads of a page read by one
+    workgroup together instead of one workgroup per (page, head)."""
     from paged_kv_cache_110_amd.probe import pages_of
 
     pages = pages_of(meta["block_tables"], meta["context_lens"], plan.block_size).to("cuda")
@@ -204,13 +206,15 @@ def paged_read_ceiling(torch, probe, plan, meta, views, runs: int = 20) -> dict:
 
     def run(i):
         kc, vc = views[i % len(views)]
-        probe.paged_read(kc, vc, pages, sink, nontemporal=True)
+        probe.paged_read(kc, vc, pages, sink, nontemporal=True, group_heads=group_heads)
 
     for i in range(2):
         run(i)
     ms = timed_calls(torch, run, runs)
     nbytes = kv_bytes(plan)
-    return dict(kernel="paged_read_kernel<non-temporal loads> (libpkv_probe)", bytes=nbytes, ms=spread(ms),
+    form = "heads of a page together" if group_heads else "one workgroup per (page, head)"
+    return dict(kernel=f"paged_read_kernel<non-temporal loads, {form}> (libpkv_probe)", bytes=nbytes,
+                ms=spread(ms),
                 gb_per_s=round(nbytes / statistics.fmean(ms) / 1e6, 1),
                 pages=int(pages.shape[0]))
 
@@ -387,6 +391,8 @@ def run_workload(name, steps, warmup, pools, torch, pkv, probe, log, cpu_budget=
     if plan.kind == "decode":
         views = [(t.k_cache(l), t.v_cache(l)) for l in range(L) for t in tens]
         res["read_ceiling"] = paged_read_ceiling(torch, probe, plan, meta, views)
+        res["read_ceiling_grouped"] = paged_read_ceiling(torch, probe, plan, meta, views,
+                                                         group_heads=plan.H_kv <= 16)
     if cpu_budget is not None:
         leg = oracle_decode_leg if plan.kind == "decode" else oracle_prefill_leg
         res["cpu"] = leg(plan, tens, outs, cpu_budget, log)
@@ -409,6 +415,7 @@ def summarize(res, ceilings) -> dict:
         per_step = (per_call + store_bytes(plan)) * plan.layers
         achieved = per_call / mean_s / 1e9
         rc = res["read_ceiling"]
+        rg = res["read_ceiling_grouped"]
         out.update(
             gb_per_s=round(per_step / (res["ms_per_step"] * 1e-3) / 1e9, 2),
             tokens_per_s=round(plan.B / (res["ms_per_step"] * 1e-3), 1),
@@ -419,7 +426,9 @@ def summarize(res, ceilings) -> dict:
                           frac=round(achieved / HBM_PEAK_GBS, 4), bytes_per_launch=per_call,
                           read_ceiling=rc["gb_per_s"],
                           frac_of_read_ceiling=round(achieved / rc["gb_per_s"], 4),
-                          read_ceiling_probe=rc))
+                          read_ceiling_probe=rc,
+                          read_ceiling_heads_together=rg["gb_per_s"],
+                          frac_of_read_ceiling_heads_together=round(achieved / rg["gb_per_s"], 4)))
         traffic = measured_traffic(plan.name)
         out["roofline"].update(
             traffic=None if traffic is None else round(traffic),

@@ -37,14 +37,18 @@ extern "C" {
  *   sink              one uint32
  *   nontemporal       nonzero: the loads carry the non-temporal hint, as the
  *                     decode's K/V loads do
- * One workgroup of 64 lanes per (page, head).
+ *   group_heads       0: one workgroup of 64 lanes per (page, head), the
+ *                     decode's pattern; nonzero: one workgroup of H_kv
+ *                     wavefronts per page, one head each, so the heads of the
+ *                     same token rows are read by one CU together
  * PKV_EINVAL: null pointers, num_pages < 1, num_blocks < 1, H_kv < 1, d not
- * 64 or 128, block_size not a power of two >= 16, misaligned caches.
+ * 64 or 128, block_size not a power of two >= 16, misaligned caches,
+ * group_heads with H_kv > 16.
  */
 int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t* pages,
                          int32_t num_pages, int32_t num_blocks, int32_t H_kv, int32_t d,
                          int32_t block_size, uint32_t* sink, int32_t nontemporal,
-                         hipStream_t stream);
+                         int32_t group_heads, hipStream_t stream);
 
 /*
  * Plain streaming read of `bytes` bytes (a multiple of 16, 16-byte aligned

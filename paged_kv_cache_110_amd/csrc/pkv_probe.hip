@@ -33,7 +33,7 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 // V, two 16-token tiles per round.  A row of one head is d bf16 = d/8 lanes of
 // 16 bytes, so one load instruction covers 64 / (d/8) rows.
 template <int D, bool NT>
-__global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restrict__ k_cache,
+__global__ __launch_bounds__(1024) void paged_read_kernel(const uint16_t* __restrict__ k_cache,
                                                         const uint16_t* __restrict__ v_cache,
                                                         const int32_t* __restrict__ pages,
                                                         int32_t num_blocks, int32_t H_kv,
@@ -42,12 +42,15 @@ __global__ __launch_bounds__(64) void paged_read_kernel(const uint16_t* __restri
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   constexpr int kLoadsPerTile = 16 / kRowsPerLoad;
-  const int page = blockIdx.x / H_kv;
-  const int h = blockIdx.x - page * H_kv;
+  // one wavefront per (page, head); a workgroup holds one of them, or all
+  // H_kv heads of one page (then they read the page's rows together)
+  const int unit = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int page = unit / H_kv;
+  const int h = unit - page * H_kv;
   const int32_t block = pages[2 * page];
   const int32_t used = min(pages[2 * page + 1], block_size);
   if (block < 0 || block >= num_blocks) return;  // a bad entry reads nothing
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int r0 = lane / kLanesPerRow;
   const int64_t row = (int64_t)H_kv * D;
   const int64_t base = (int64_t)block * block_size * row + h * D + (lane % kLanesPerRow) * 8;
@@ -161,28 +164,30 @@ extern "C" {
 int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t* pages,
                          int32_t num_pages, int32_t num_blocks, int32_t H_kv, int32_t d,
                          int32_t block_size, uint32_t* sink, int32_t nontemporal,
-                         hipStream_t stream) {
+                         int32_t group_heads, hipStream_t stream) {
   if (!k_cache || !v_cache || !pages || !sink || num_pages < 1 || num_blocks < 1 || H_kv < 1)
     return 1;
+  if (group_heads && H_kv > 16) return 1;
   if (d != 64 && d != 128) return 1;
   if (block_size < 16 || (block_size & (block_size - 1))) return 1;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return 1;
   if ((int64_t)num_pages * H_kv > INT32_MAX) return 1;
-  const dim3 grid((unsigned)(num_pages * H_kv));
+  const dim3 grid((unsigned)(group_heads ? num_pages : num_pages * H_kv));
+  const dim3 block(group_heads ? 64 * H_kv : 64);
   const auto* kc = static_cast<const uint16_t*>(k_cache);
   const auto* vc = static_cast<const uint16_t*>(v_cache);
   const bool nt = nontemporal != 0;
   if (d == 128 && nt)
-    hipLaunchKernelGGL((paged_read_kernel<128, true>), grid, dim3(64), 0, stream, kc, vc, pages,
+    hipLaunchKernelGGL((paged_read_kernel<128, true>), grid, block, 0, stream, kc, vc, pages,
                        num_blocks, H_kv, block_size, sink);
   else if (d == 128)
-    hipLaunchKernelGGL((paged_read_kernel<128, false>), grid, dim3(64), 0, stream, kc, vc, pages,
+    hipLaunchKernelGGL((paged_read_kernel<128, false>), grid, block, 0, stream, kc, vc, pages,
                        num_blocks, H_kv, block_size, sink);
   else if (nt)
-    hipLaunchKernelGGL((paged_read_kernel<64, true>), grid, dim3(64), 0, stream, kc, vc, pages,
+    hipLaunchKernelGGL((paged_read_kernel<64, true>), grid, block, 0, stream, kc, vc, pages,
                        num_blocks, H_kv, block_size, sink);
   else
-    hipLaunchKernelGGL((paged_read_kernel<64, false>), grid, dim3(64), 0, stream, kc, vc, pages,
+    hipLaunchKernelGGL((paged_read_kernel<64, false>), grid, block, 0, stream, kc, vc, pages,
                        num_blocks, H_kv, block_size, sink);
   return status(hipGetLastError());
 }

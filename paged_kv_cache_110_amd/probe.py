@@ -26,7 +26,7 @@ def load() -> ctypes.CDLL:
                           "`python -m paged_kv_cache_110_amd.build` (hipcc, gfx950)")
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    lib.pkv_probe_paged_read.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, I32, P]
+    lib.pkv_probe_paged_read.argtypes = [P, P, P, I32, I32, I32, I32, I32, P, I32, I32, P]
     lib.pkv_probe_read.argtypes = [P, I64, P, I32, P]
     lib.pkv_probe_copy.argtypes = [P, P, I64, P]
     lib.pkv_probe_mfma.argtypes = [P, I32, I32, I32, I32, I32, P]
@@ -57,11 +57,11 @@ def pages_of(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size:
 
 
 def paged_read(k_cache, v_cache, pages: torch.Tensor, sink: torch.Tensor,
-               nontemporal: bool = True) -> None:
+               nontemporal: bool = True, group_heads: bool = False) -> None:
     nb, bs, H_kv, d = k_cache.shape
     _check("pkv_probe_paged_read", load().pkv_probe_paged_read(
         k_cache.data_ptr(), v_cache.data_ptr(), pages.data_ptr(), pages.shape[0], nb, H_kv, d, bs,
-        sink.data_ptr(), int(nontemporal), _stream()))
+        sink.data_ptr(), int(nontemporal), int(group_heads), _stream()))
 
 
 def read(src: torch.Tensor, sink: torch.Tensor, nontemporal: bool = False) -> None:

@@ -351,11 +351,12 @@ def test_probe_library_exports_and_argument_checks():
     buf = ctypes.create_string_buffer(4096 + 16)
     p = (ctypes.addressof(buf) + 15) // 16 * 16
     # paged read: d, block size, null pointers, empty page list, misaligned cache
-    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 8, 96, 256, p, 1, None) == 1
-    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 8, 128, 48, p, 0, None) == 1
-    assert lib.pkv_probe_paged_read(None, p, p, 1, 4, 8, 128, 256, p, 1, None) == 1
-    assert lib.pkv_probe_paged_read(p, p, p, 0, 4, 8, 128, 256, p, 1, None) == 1
-    assert lib.pkv_probe_paged_read(p + 2, p, p, 1, 4, 8, 128, 256, p, 1, None) == 1
+    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 8, 96, 256, p, 1, 0, None) == 1
+    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 8, 128, 48, p, 0, 1, None) == 1
+    assert lib.pkv_probe_paged_read(None, p, p, 1, 4, 8, 128, 256, p, 1, 0, None) == 1
+    assert lib.pkv_probe_paged_read(p, p, p, 0, 4, 8, 128, 256, p, 1, 0, None) == 1
+    assert lib.pkv_probe_paged_read(p + 2, p, p, 1, 4, 8, 128, 256, p, 1, 0, None) == 1
+    assert lib.pkv_probe_paged_read(p, p, p, 1, 4, 32, 128, 256, p, 1, 1, None) == 1  # grouped, H_kv > 16
     # read / copy: sizes that are not whole 16-byte chunks, misaligned buffers
     assert lib.pkv_probe_read(p, 24, p, 1, None) == 1
     assert lib.pkv_probe_read(p + 8, 32, p, 0, None) == 1
