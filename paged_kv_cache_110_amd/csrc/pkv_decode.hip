@@ -854,6 +854,89 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
+// The merge for G = 8, one wavefront per (sequence, KV head) segment
+// instead of one per output row: the segment's record and the sequence's
+// length are read once for its 8 rows, lane group g (8 lanes, D / 8 elements
+// each) combines query head g, and every lane keeps four pieces' loads in
+// flight.  Pieces are combined in share order, as in decode_merge_kernel, so
+// the result is deterministic.  (At G = 2 this form was slower than one
+// wavefront per row: half as many rows per wavefront fill fewer lanes.)
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_seg8_kernel(
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
+    const SegInfo* __restrict__ ws_seg, int32_t* __restrict__ queue,
+    const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out, int32_t B, int32_t H_kv,
+    int32_t max_shares) {
+  constexpr int G = 8;
+  constexpr int LPR = 64 / G;   // lanes per query head
+  constexpr int EPL = D / LPR;  // elements per lane
+  constexpr int KB = 4;         // pieces in flight
+  if (blockIdx.x == 0 && threadIdx.x == 0) *queue = 0;
+  const int lane = threadIdx.x % 64;
+  const int g = lane / LPR;
+  const int sub = lane % LPR;
+  const int64_t seg = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // b * H_kv + h
+  if (seg >= (int64_t)B * H_kv) return;
+  const int b = (int)(seg / H_kv);
+  const int32_t len = context_lens[b];
+  const SegInfo info = ws_seg[seg];
+  asm volatile("" ::"v"(info.k_first), "v"(info.k_last));
+  uint16_t* op = out + (seg * G + g) * D + sub * EPL;  // row b * H_q + h * G + g
+  if (len <= 0) {
+#pragma unroll
+    for (int w = 0; w < EPL / 8; ++w) st16(op + 8 * w, u32x4{0u, 0u, 0u, 0u});
+    return;
+  }
+  if (info.k_last <= info.k_first) return;  // one piece: written by the decode kernel
+  if (info.k_first < 0 || info.k_last >= max_shares) return;  // not from this call's layout
+  const int nparts = info.k_last - info.k_first + 1;
+  auto prow = [&](int p) -> int64_t {
+    const int64_t k = (int64_t)info.k_first + p;
+    return (k * 2 + (p == 0 ? 1 : 0)) * G + g;
+  };
+  float mg = -INFINITY, lg = 0.f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += KB) {
+    float2 st[KB];
+    f32x4 v[KB][EPL / 4];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {  // unconditional loads (a piece past the end reads piece 0)
+      const int p = p0 + j;
+      const int64_t r = prow(p < nparts ? p : 0);
+      st[j] = *reinterpret_cast<const float2*>(ws_ml + 2 * r);
+      const float* src = ws_acc + r * D + sub * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL / 4; ++e) v[j][e] = *reinterpret_cast<const f32x4*>(src + 4 * e);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any use
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      // piece 0 always exists and its max is finite, so mg is finite before
+      // any piece past the end, which weighs 0
+      const bool in = p0 + j < nparts;
+      const float mj = in ? st[j].x : -INFINITY;
+      const float mn = fmaxf(mg, mj);
+      const float a = fast_exp2(mg - mn);  // 0 for the first piece
+      const float w = fast_exp2(mj - mn);
+      lg = lg * a + (in ? st[j].y : 0.f) * w;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = o[e] * a + v[j][e / 4][e % 4] * w;
+      mg = mn;
+    }
+  }
+  const float inv = 1.0f / lg;
+#pragma unroll
+  for (int w = 0; w < EPL / 8; ++w) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      r[k] = pack_bf16x2(o[8 * w + 2 * k] * inv, o[8 * w + 2 * k + 1] * inv);
+    st16(op + 8 * w, r);
+  }
+}
+
 // ----------------------------------------------------------------- host side
 
 static int ilog2(int x) {
@@ -984,6 +1067,16 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   if (e != hipSuccess) return e;
   const int64_t nrows = (int64_t)B * H_q;
   const int32_t max_shares = (int32_t)ShareSchedule::max_shares(plan.num_waves);
+  if (G == 8) {
+    const dim3 sgrid((unsigned)(((int64_t)B * H_kv + 3) / 4));
+    if (d == 128)
+      hipLaunchKernelGGL(decode_merge_seg8_kernel<128>, sgrid, dim3(256), 0, stream, wa, wm, wseg,
+                         queue, context_lens, out, B, H_kv, max_shares);
+    else
+      hipLaunchKernelGGL(decode_merge_seg8_kernel<64>, sgrid, dim3(256), 0, stream, wa, wm, wseg,
+                         queue, context_lens, out, B, H_kv, max_shares);
+    return hipGetLastError();
+  }
   dim3 mgrid((unsigned)((nrows + 3) / 4));
   if (d == 128)
     hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(256), 0, stream, wa, wm, wseg,
