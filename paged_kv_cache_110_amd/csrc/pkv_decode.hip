@@ -854,23 +854,23 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
-// The merge for G = 8, one wavefront per (sequence, KV head) segment
+// The merge for wide groups, one wavefront per (sequence, KV head) segment
 // instead of one per output row: the segment's record and the sequence's
-// length are read once for its 8 rows, lane group g (8 lanes, D / 8 elements
-// each) combines query head g, and every lane keeps four pieces' loads in
-// flight.  Pieces are combined in share order, as in decode_merge_kernel, so
-// the result is deterministic.  (At G = 2 this form was slower than one
-// wavefront per row: half as many rows per wavefront fill fewer lanes.)
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_seg8_kernel(
+// length are read once for its G rows, lane group g (64 / G lanes, G * D / 64
+// elements each) combines query head g, and every lane keeps four pieces'
+// loads in flight.  Pieces are combined in share order, as in
+// decode_merge_kernel, so the result is deterministic.  Used at G = 8 (at
+// G = 4 it measured the same as one wavefront per row, at G = 2 slower).
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_merge_seg_kernel(
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
     const SegInfo* __restrict__ ws_seg, int32_t* __restrict__ queue,
     const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out, int32_t B, int32_t H_kv,
     int32_t max_shares) {
-  constexpr int G = 8;
   constexpr int LPR = 64 / G;   // lanes per query head
   constexpr int EPL = D / LPR;  // elements per lane
   constexpr int KB = 4;         // pieces in flight
+  static_assert(EPL % 8 == 0, "whole 16-byte stores per lane");
   if (blockIdx.x == 0 && threadIdx.x == 0) *queue = 0;
   const int lane = threadIdx.x % 64;
   const int g = lane / LPR;
@@ -1070,10 +1070,10 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   if (G == 8) {
     const dim3 sgrid((unsigned)(((int64_t)B * H_kv + 3) / 4));
     if (d == 128)
-      hipLaunchKernelGGL(decode_merge_seg8_kernel<128>, sgrid, dim3(256), 0, stream, wa, wm, wseg,
+      hipLaunchKernelGGL((decode_merge_seg_kernel<128, 8>), sgrid, dim3(256), 0, stream, wa, wm, wseg,
                          queue, context_lens, out, B, H_kv, max_shares);
     else
-      hipLaunchKernelGGL(decode_merge_seg8_kernel<64>, sgrid, dim3(256), 0, stream, wa, wm, wseg,
+      hipLaunchKernelGGL((decode_merge_seg_kernel<64, 8>), sgrid, dim3(256), 0, stream, wa, wm, wseg,
                          queue, context_lens, out, B, H_kv, max_shares);
     return hipGetLastError();
   }
