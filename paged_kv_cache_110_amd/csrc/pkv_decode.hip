@@ -71,12 +71,17 @@ struct SegInfo {
   int32_t pad0, pad1;
 };
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// Inclusive prefix sum over the 64 lanes on DPP: shifts by 1, 2, 4 and 8
+// within each row of 16 lanes, then each row adds the last lane of the rows
+// before it (row_bcast:15, then row_bcast:31).  Lanes a shift would read from
+// outside their row add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return x;
 }
 
@@ -139,16 +144,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     }
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int n = cnt[c] * H_kv;
-      const int incl = wave_incl_scan(n, lane) + T;
-      pre[c * 64 + lane] = incl - n;
-      T = uniform(__shfl(incl, 63, 64));
+      if (c * 64 < B) {
+        const int n = cnt[c] * H_kv;
+        const int incl = wave_incl_scan(n) + T;
+        pre[c * 64 + lane] = incl - n;
+        T = uniform(__shfl(incl, 63, 64));
+      } else {
+        pre[c * 64 + lane] = T;  // no sequences here: the offsets stay at T
+      }
     }
     if (lane == 0) pre[kSeqCache] = T;
     for (int b0 = kSeqCache; b0 < B; b0 += 64) {
       const int b = b0 + lane;
       const int n = b < B ? tiles_of(context_lens[b]) * H_kv : 0;
-      T += uniform(__shfl(wave_incl_scan(n, lane), 63, 64));
+      T += uniform(__shfl(wave_incl_scan(n), 63, 64));
     }
   }
 
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       for (int b0 = kSeqCache; b0 < B; b0 += 64) {
         const int bb = b0 + lane;
         const int n = bb < B ? tiles_of(context_lens[bb]) * H_kv : 0;
-        const int incl = wave_incl_scan(n, lane) + run;
+        const int incl = wave_incl_scan(n) + run;
         const int excl = incl - n;
         const unsigned long long hit = __ballot(n > 0 && excl <= u && u < incl);
         if (hit) {
