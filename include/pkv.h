@@ -149,8 +149,8 @@ size_t pkv_decode_workspace_size(int32_t B, int32_t H_q, int32_t H_kv, int32_t d
  * The causal mask of the pages' call is a no-op for one query per sequence.
  * The work (every 16-token tile of every (sequence, KV head)) is cut into
  * shares: one static share per resident wavefront of the device (all of the
- * work for calls of up to 64 tiles per wavefront, else 3/5 of it up to 128
- * tiles per wavefront and 2/5 above), then shrinking shares that wavefronts
+ * work for calls of up to 64 tiles per wavefront, else 7/10 of it (4/5 for
+ * G >= 4) up to 128 tiles per wavefront and 2/5 above), then shrinking shares that wavefronts
  * take from an atomic counter as they finish, so all of them stop at nearly
  * the same time.  K and V are read with non-temporal loads (each byte once).
  * Pieces of a sequence that span shares are merged with a log-sum-exp rescale
@@ -168,6 +168,36 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
                       int32_t H_q, int32_t H_kv, int32_t d, int32_t num_blocks,
                       int32_t block_size, int32_t max_blocks_per_seq, float softmax_scale,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+
+/*
+ * The store of a decode step fused into its attention call (devpress page,
+ * KV-cache write then "PagedAttention是如何实现的"): the same result as
+ * pkv_store of each sequence's new token followed by pkv_decode, in one
+ * launch fewer.  Sequence b's new token sits at position p = context_lens[b] - 1
+ * (its slot: row p % block_size of block block_tables[b][p / block_size]);
+ * its K/V rows are key[b] and value[b].  The call writes them there, bit for
+ * bit, and attends over positions [0, context_lens[b]) as pkv_decode does
+ * (the new token's row is read from key/value, not from the cache).
+ * Sequences with context_lens[b] <= 0 store nothing and give zero rows.
+ *   key, value    device, [B, H_kv, d] bf16; head and d contiguous, sequence
+ *                 stride key_stride / value_stride elements (>= H_kv*d,
+ *                 multiple of 8), e.g. views into a fused QKV projection.
+ *   the rest      as pkv_decode (same workspace size).
+ * Preconditions as pkv_decode's, plus: the new token's block belongs to
+ * sequence b alone (no other sequence of the call reads it), as a block that
+ * is being written never holds a shared prefix.
+ * PKV_EINVAL: pkv_decode's cases, null key/value, a stride below H_kv*d or
+ * not a multiple of 8, key/value not 16-byte aligned.
+ * PKV_EUNSUPPORTED: as pkv_decode.
+ */
+pkv_status pkv_store_decode(void* out, const void* q, const void* key, int64_t key_stride,
+                            const void* value, int64_t value_stride, void* k_cache,
+                            void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv,
+                            int32_t d, int32_t num_blocks, int32_t block_size,
+                            int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Varlen causal prefill over the paged cache (devpress page, "如何适配不同请求
@@ -420,13 +450,22 @@ pkv_status pkv_prepare_metadata_device(int32_t B, const int32_t* idx_mapping,
 typedef struct pkv_decode_graph pkv_decode_graph;
 
 /*
- * The step a graph set captures.  All pointers are device pointers except
- * the per-layer arrays themselves (host arrays of `layers` device pointers,
- * read at create time; the graphs bake in the device addresses, so the
- * buffers must stay allocated and in place while the graph set exists).
- *   slot_mapping   [max_batch] int32   rows [0, batch) written by the caller
- *   context_lens   [max_batch] int32   before each replay; the replay writes
- *                                      the padding rows [batch, bucket)
+ * The step a graph set captures: for each layer l, one pkv_store_decode call
+ * over the batch's rows (row b's new token, key[l][b] and value[l][b], goes to
+ * position context_lens[b] - 1 through block_tables, the slot the pages'
+ * decode metadata puts in slot_mapping, and is attended with the rest).  All
+ * pointers are device pointers except the per-layer arrays themselves (host
+ * arrays of `layers` device pointers, read at create time; the graphs bake in
+ * the device addresses, so the buffers must stay allocated and in place while
+ * the graph set exists).
+ *   slot_mapping   [max_batch] int32   the batch's slots (rows [0, batch)
+ *                                      written by the caller, for its own
+ *                                      use: the step stores through the
+ *                                      table); the replay sets the padding
+ *                                      rows [batch, bucket) to -1
+ *   context_lens   [max_batch] int32   rows [0, batch) written by the caller
+ *                                      before each replay; the replay writes
+ *                                      0 to the padding rows [batch, bucket)
  *   block_tables   [max_batch, max_blocks_per_seq] int32
  *   q[l], out[l]   [max_batch, H_q, d] bf16, contiguous
  *   key[l], value[l]   [max_batch, H_kv, d] bf16 rows key_stride /
@@ -474,8 +513,8 @@ int32_t pkv_decode_graph_bucket(int32_t max_batch, int32_t batch);
  * on a stream of its own and waits for that stream.  On success *graph owns
  * the graphs; release them with pkv_decode_graph_destroy.
  * PKV_EINVAL: null pointers, layers < 1, max_batch outside [1, 512], a
- * workspace smaller than needed, or any argument pkv_store / pkv_decode
- * would reject.  PKV_EUNSUPPORTED as for pkv_decode.  PKV_ELAUNCH: the HIP
+ * workspace smaller than needed, or any argument pkv_store_decode would
+ * reject.  PKV_EUNSUPPORTED as for pkv_decode.  PKV_ELAUNCH: the HIP
  * runtime failed (nothing is left allocated).
  */
 pkv_status pkv_decode_graph_create(const pkv_decode_step* step, pkv_decode_graph** graph);
@@ -496,8 +535,8 @@ pkv_status pkv_decode_graph_replay(pkv_decode_graph* graph, int32_t batch, hipSt
 
 /*
  * The same step issued eagerly on `stream` (the pages' enforce_eager branch):
- * for each layer, pkv_store and pkv_decode over rows [0, batch) of the
- * step's buffers, with no padding.  Not blocking.  Same errors as
+ * for each layer, pkv_store_decode over rows [0, batch) of the step's
+ * buffers, with no padding.  Not blocking.  Same errors as
  * pkv_decode_graph_create for the step, plus batch outside [0, max_batch].
  */
 pkv_status pkv_decode_step_run(const pkv_decode_step* step, int32_t batch, hipStream_t stream);

@@ -35,7 +35,7 @@ import torch
 from ._lib import EXPORTS, LIB_PATH, DecodeStep, PkvError, check, load
 
 __all__ = [
-    "prepare_metadata", "store", "decode", "decode_workspace_size", "prefill_varlen",
+    "prepare_metadata", "store", "decode", "store_decode", "decode_workspace_size", "prefill_varlen",
     "prefill_varlen_packed", "pack_row_writes", "apply_row_writes", "StagedWrites",
     "prepare_metadata_device", "sample_gumbel", "sample_gumbel_noalloc", "sample_workspace_size",
     "graph_bucket", "DecodeGraph", "PkvError", "LIB_PATH", "EXPORTS",
@@ -164,6 +164,42 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         B, H_q, H_kv, d, nb, bs, maxb, scale, _ptr(workspace), have, _stream(stream)))
     return out
 
+
+
+def store_decode(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                 softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The decode step's store fused into its attention: key/value [B, H_kv, d] (sequence
+    b's new token, stored at position context_lens[b] - 1) and q [B, H_q, d] -> out."""
+    nb, bs, H_kv, d = _cache_geometry(k_cache, v_cache)
+    _need(q.dim() == 3 and q.shape[2] == d and q.dtype == torch.bfloat16 and q.is_cuda
+          and q.is_contiguous(), "q must be a contiguous bf16 GPU tensor [B, H_q, d]")
+    B, H_q = int(q.shape[0]), int(q.shape[1])
+    _need(key.dim() == 3 and key.shape == value.shape and tuple(key.shape) == (B, H_kv, d),
+          "key/value must be [B, H_kv, d] matching q and the cache")
+    _need(key.dtype == torch.bfloat16 and value.dtype == torch.bfloat16, "key/value bfloat16")
+    _need(key.is_cuda and value.is_cuda, "key/value must be GPU tensors")
+    _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1
+          and value.stride(1) == d, "key/value head and d dims must be contiguous")
+    _dev_i32(block_tables, "block_tables")
+    _dev_i32(context_lens, "context_lens")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B, maxb]")
+    _need(context_lens.shape == (B,), "context_lens must be [B]")
+    maxb = int(block_tables.shape[1])
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    ws_bytes = decode_workspace_size(B, H_q, H_kv, d, bs, maxb)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    check("pkv_store_decode", load().pkv_store_decode(
+        _ptr(out), _ptr(q), _ptr(key), key.stride(0), _ptr(value), value.stride(0),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        B, H_q, H_kv, d, nb, bs, maxb, scale, _ptr(workspace), have, _stream(stream)))
+    return out
 
 def prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                    block_tables: torch.Tensor, cu_seqlens_q: torch.Tensor,

@@ -21,6 +21,7 @@ EXPORTS = (
     "pkv_store",
     "pkv_decode_workspace_size",
     "pkv_decode",
+    "pkv_store_decode",
     "pkv_prefill_varlen",
     "pkv_prefill_varlen_packed",
     "pkv_sample_workspace_size",
@@ -88,6 +89,9 @@ def load() -> ctypes.CDLL:
     lib.pkv_decode_workspace_size.restype = SZ
     lib.pkv_decode.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F, P, SZ, P]
     lib.pkv_decode.restype = ctypes.c_int
+    lib.pkv_store_decode.argtypes = [P, P, P, I64, P, I64, P, P, P, P, I32, I32, I32, I32, I32,
+                                     I32, I32, F, P, SZ, P]
+    lib.pkv_store_decode.restype = ctypes.c_int
     lib.pkv_prefill_varlen.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32,
                                        I32, I32, I32, F, P]
     lib.pkv_prefill_varlen.restype = ctypes.c_int

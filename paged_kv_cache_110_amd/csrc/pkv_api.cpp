@@ -177,7 +177,39 @@ pkv_status pkv_decode(void* out, const void* q, const void* k_cache, const void*
       static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_tables,
       context_lens, B, H_q, H_kv, d, num_blocks, block_size, max_blocks_per_seq, softmax_scale,
-      workspace, plan, stream));
+      workspace, plan, pkv::NewToken{}, stream));
+}
+
+pkv_status pkv_store_decode(void* out, const void* q, const void* key, int64_t key_stride,
+                            const void* value, int64_t value_stride, void* k_cache,
+                            void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv,
+                            int32_t d, int32_t num_blocks, int32_t block_size,
+                            int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (B <= 0 || !context_lens || !isfinite(softmax_scale)) return PKV_EINVAL;
+  if (!key || !value) return PKV_EINVAL;
+  pkv_status st = check_attention(out, q, k_cache, v_cache, block_tables, H_q, H_kv, d,
+                                  num_blocks, block_size, max_blocks_per_seq);
+  if (st != PKV_OK) return st;
+  const int64_t row = (int64_t)H_kv * d;
+  if (key_stride < row || value_stride < row || key_stride % 8 || value_stride % 8)
+    return PKV_EINVAL;
+  if (!aligned16(key) || !aligned16(value)) return PKV_EINVAL;
+  if ((int64_t)B * H_kv > INT32_MAX) return PKV_EINVAL;
+  if (!decode_units_fit(B, H_kv, block_size, max_blocks_per_seq)) return PKV_EUNSUPPORTED;
+  const pkv::DecodePlan plan = pkv::decode_plan(B, H_q, H_kv, d, block_size, max_blocks_per_seq);
+  if (plan.num_waves <= 0) return PKV_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
+    return PKV_EINVAL;
+  const pkv::NewToken nt{static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                         key_stride, value_stride, static_cast<uint16_t*>(k_cache),
+                         static_cast<uint16_t*>(v_cache)};
+  return launch_status(pkv::launch_decode(
+      static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_tables,
+      context_lens, B, H_q, H_kv, d, num_blocks, block_size, max_blocks_per_seq, softmax_scale,
+      workspace, plan, nt, stream));
 }
 
 pkv_status pkv_prefill_varlen(void* out, const void* q, const void* k_cache,

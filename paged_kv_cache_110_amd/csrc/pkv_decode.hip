@@ -71,6 +71,7 @@ struct SegInfo {
   int32_t pad0, pad1;
 };
 
+
 // Inclusive prefix sum over the 64 lanes on DPP: shifts by 1, 2, 4 and 8
 // within each row of 16 lanes, then each row adds the last lane of the rows
 // before it (row_bcast:15, then row_bcast:31).  Lanes a shift would read from
@@ -89,14 +90,14 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 // Unit counts fit in int32: the host rejects shapes where
 // B * H_kv * ceil(max_blocks_per_seq * block_size / 16) could exceed INT32_MAX.
-template <int D, int G, int EPL, int NBUF, int WPE, bool MF>
+template <int D, int G, int EPL, int NBUF, int WPE, bool MF, bool FUSE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, uint16_t* __restrict__ out,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, SegInfo* __restrict__ ws_seg,
     int32_t* __restrict__ queue, int32_t B, int32_t H_kv, int32_t num_blocks, int32_t bs_log2,
-    int32_t maxb, float scale_log2e) {
+    int32_t maxb, float scale_log2e, NewToken nt_in) {
   constexpr int LPT = D / EPL;           // lanes per token
   constexpr int TPI = 64 / LPT;          // tokens side by side in a wave
   constexpr int TPL = kDecodeTile / TPI; // tokens per lane per tile
@@ -106,6 +107,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 
   __shared__ int pre[kSeqCache + 1];  // units of the sequences before b
   __shared__ int lenc[kSeqCache];     // clamped context length of b
+  // fused store: whether sequence b's new token lies inside its table
+  // (context_lens[b] <= the table's capacity); a clamped length stores nothing
+  __shared__ int8_t newok[FUSE ? kSeqCache : 1];
   // MFMA form: the tile being computed, K then V, 16 rows of D bf16 each with
   // swizzled 16-byte chunks (mf_off)
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[MF ? 2 * kDecodeTile * D : 8];
@@ -138,7 +142,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int b = c * 64 + lane;
-      const int len = b < B ? clamp_len(context_lens[b]) : 0;
+      int len;
+      if constexpr (FUSE) {
+        const int raw = b < B ? context_lens[b] : 0;
+        len = clamp_len(raw);
+        newok[c * 64 + lane] = raw <= cap;
+      } else {
+        len = b < B ? clamp_len(context_lens[b]) : 0;
+      }
       lenc[c * 64 + lane] = len;
       cnt[c] = (len + kDecodeTile - 1) / kDecodeTile;
     }
@@ -287,11 +298,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     kEnd = 4,          // last tile of a piece
     kBeganBefore = 8,  // the piece's segment started in an earlier share
     kSegEnd = 16,      // the piece holds the segment's last tile
-    kLast = 32         // the wavefront's last tile
+    kLast = 32,        // the wavefront's last tile
+    kNewRow = 64       // the segment's last tile of a call with the store fused in
   };
   struct Meta {
     int b, h, flags, k;
     int rows;  // valid key rows of the tile (0 for an empty tile)
+    int64_t new_row;  // kNewRow: element offset of the new token's rows in the caches
   };
 
   // q of the next pieces is loaded by the load cursor when it reaches their
@@ -372,14 +385,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     const uint16_t* vt = v_cache + row0 * rs + (int64_t)L.h * D;
     const int last = L.len - 1 - t;
     mt.rows = uniform(blk_ok ? last + 1 : 0);
+    // With the store fused in, the segment's last tile (also when re-read as
+    // an empty step) takes its last row from the new token, so the kernel
+    // never reads the cache row it writes.
+    bool from_new = false;
+    if constexpr (FUSE) {
+      if (L.j + 1 == L.nt)
+        from_new = L.b < kSeqCache ? uniform(newok[L.b]) != 0 : context_lens[L.b] <= cap;
+    }
+    if (from_new && real && blk_ok) {
+      mt.flags |= kNewRow;
+      mt.new_row = (row0 + last) * rs + (int64_t)L.h * D;
+    }
+    const uint16_t* kn = from_new ? nt_in.key + (int64_t)L.b * nt_in.key_stride + (int64_t)L.h * D : kt;
+    const uint16_t* vn = from_new ? nt_in.value + (int64_t)L.b * nt_in.value_stride + (int64_t)L.h * D : vt;
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       const int r = grp + i * TPI;
+      // rows past the last one re-read it (weight 0): from the new token too,
+      // since its cache row is not written yet
+      const bool nr = from_new && r >= last;
       const int off = (r <= last ? r : last) * rs;
+      const uint16_t* kp = nr ? kn : kt + off;
+      const uint16_t* vp = nr ? vn : vt + off;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        kx[i][w] = ld16_stream(kt + off + dofs(w));
-        vx[i][w] = ld16_stream(vt + off + dofs(w));
+        kx[i][w] = ld16_stream(kp + dofs(w));
+        vx[i][w] = ld16_stream(vp + dofs(w));
       }
     }
     if (real && !switch_pending) step_unit(L);
@@ -710,6 +742,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     }
   };
 
+  // The fused store: the lanes holding the tile's last row (the new token,
+  // read from the new K/V input) write it into the caches.
+  auto store_new_row = [&](const u32x4 (&kx)[TPL][NW], const u32x4 (&vx)[TPL][NW], const Meta& mt) {
+#pragma unroll
+    for (int i = 0; i < TPL; ++i) {
+      if (grp + i * TPI != mt.rows - 1) continue;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        st16(nt_in.k_cache + mt.new_row + dofs(w), kx[i][w]);
+        st16(nt_in.v_cache + mt.new_row + dofs(w), vx[i][w]);
+      }
+    }
+  };
+
   // Ring of NBUF register buffers; the loop is unrolled NBUF times so every
   // buffer index is a compile-time constant (no register copies).
   u32x4 kbuf[NBUF][TPL][NW], vbuf[NBUF][TPL][NW];
@@ -729,6 +775,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       if ((mt.flags & (kValid | kBegin)) == (kValid | kBegin)) begin_segment(mt);
       load_tile(kbuf[nxt], vbuf[nxt], meta[nxt], grab[nxt]);
       if (mt.flags & kValid) {
+        if (FUSE && (mt.flags & kNewRow)) store_new_row(kbuf[u], vbuf[u], mt);
         compute_tile(kbuf[u], vbuf[u], mt.rows);
         if (mt.flags & kEnd) end_segment(mt);
         if (mt.flags & kLast) done = true;
@@ -966,8 +1013,8 @@ static int resident_waves() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, EPL, NBUF, WPE, MF>, 64,
-                                                     0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, G, EPL, NBUF, WPE, MF, false>,
+                                                     64, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 8;
     cached[dev] = cus * per_cu;
@@ -1048,10 +1095,17 @@ struct DecodeLaunch {
   int32_t* queue;
   int32_t B, H_kv, nb, bsl, maxb;
   float sl2e;
+  NewToken nt;
   template <int D, int G, int EPL, int NBUF, int WPE, bool MF>
   void run() {
-    hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF, WPE, MF>), grid, dim3(64), 0, st, q, kc, vc, bt, cl,
-                       out, wa, wm, wseg, queue, B, H_kv, nb, bsl, maxb, sl2e);
+    // the fused store is its own instantiation, so the plain decode keeps its
+    // registers; both have the same occupancy (two wavefronts per SIMD)
+    if (nt.key)
+      hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF, WPE, MF, true>), grid, dim3(64), 0, st, q, kc, vc,
+                         bt, cl, out, wa, wm, wseg, queue, B, H_kv, nb, bsl, maxb, sl2e, nt);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, G, EPL, NBUF, WPE, MF, false>), grid, dim3(64), 0, st, q, kc, vc,
+                         bt, cl, out, wa, wm, wseg, queue, B, H_kv, nb, bsl, maxb, sl2e, nt);
   }
 };
 
@@ -1060,7 +1114,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv,
                          int32_t d, int32_t num_blocks, int32_t block_size,
                          int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
-                         const DecodePlan& plan, hipStream_t stream) {
+                         const DecodePlan& plan, const NewToken& new_token, hipStream_t stream) {
   const int G = H_q / H_kv;
   const WorkspaceLayout wl = workspace_layout(B, H_kv, G, d, plan.num_waves);
   char* ws = static_cast<char*>(workspace);
@@ -1070,7 +1124,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   int32_t* queue = reinterpret_cast<int32_t*>(ws + wl.queue);
   DecodeLaunch lf{dim3((unsigned)plan.num_waves), stream, q, k_cache, v_cache, block_tables,
                   context_lens, out, wa, wm, wseg, queue, B, H_kv, num_blocks, ilog2(block_size),
-                  max_blocks_per_seq, softmax_scale * 1.4426950408889634f};
+                  max_blocks_per_seq, softmax_scale * 1.4426950408889634f, new_token};
   if (!dispatch(d, G, lf)) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -45,18 +45,17 @@ bool step_pointers_ok(const pkv_decode_step* s) {
   return true;
 }
 
-// Every layer's store then decode over rows [0, batch) (batch >= 1); each call
-// runs its own argument checks.
+// Every layer's store and decode over rows [0, batch) (batch >= 1), as one
+// fused launch per layer (pkv_store_decode: the new token goes to position
+// context_lens[b] - 1 through the block table, the slot_mapping entry the
+// pages' metadata gives it); each call runs its own argument checks.
 pkv_status enqueue_step(const pkv_decode_step& s, int32_t batch, hipStream_t stream) {
   for (int32_t l = 0; l < s.layers; ++l) {
-    pkv_status st = pkv_store(s.key[l], s.key_stride, s.value[l], s.value_stride, s.k_cache[l],
-                              s.v_cache[l], s.slot_mapping, batch, s.num_blocks, s.block_size,
-                              s.H_kv, s.d, stream);
-    if (st != PKV_OK) return st;
-    st = pkv_decode(s.out[l], s.q[l], s.k_cache[l], s.v_cache[l], s.block_tables,
-                    s.context_lens, batch, s.H_q, s.H_kv, s.d, s.num_blocks, s.block_size,
-                    s.max_blocks_per_seq, s.softmax_scale, s.workspace, s.workspace_bytes,
-                    stream);
+    const pkv_status st = pkv_store_decode(
+        s.out[l], s.q[l], s.key[l], s.key_stride, s.value[l], s.value_stride, s.k_cache[l],
+        s.v_cache[l], s.block_tables, s.context_lens, batch, s.H_q, s.H_kv, s.d, s.num_blocks,
+        s.block_size, s.max_blocks_per_seq, s.softmax_scale, s.workspace, s.workspace_bytes,
+        stream);
     if (st != PKV_OK) return st;
   }
   return PKV_OK;

@@ -48,6 +48,21 @@ hipError_t launch_sample(int64_t* tokens, const void* logits, bool bf16, int64_t
 constexpr int64_t kSampleScratchKeys = (int64_t)1 << 17;
 hipError_t sample_scratch_address(void** address);
 
+// The store fused into a decode call (all null otherwise): the new token of
+// sequence b, at position context_lens[b] - 1, has its K/V rows at
+// key + b * key_stride and value + b * value_stride ([H_kv, d] each).  The
+// wavefront that computes the segment's last tile reads that row from there
+// instead of the cache, and writes it into the cache (the row is in no other
+// tile, and no other wavefront of the call reads it).
+struct NewToken {
+  const uint16_t* key;
+  const uint16_t* value;
+  int64_t key_stride;
+  int64_t value_stride;
+  uint16_t* k_cache;  // the caches again, as the store's destination
+  uint16_t* v_cache;
+};
+
 // Decode launch plan: one wavefront per resident slot of the current device.
 struct DecodePlan {
   int32_t num_waves;       // 0 when the shape has no kernel
@@ -61,7 +76,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv,
                          int32_t d, int32_t num_blocks, int32_t block_size,
                          int32_t max_blocks_per_seq, float softmax_scale, void* workspace,
-                         const DecodePlan& plan, hipStream_t stream);
+                         const DecodePlan& plan, const NewToken& new_token, hipStream_t stream);
 
 // Query tiles of a prefill call (the grid's y extent, at most 65535).
 int64_t prefill_query_tiles(int32_t max_seqlen_q, int32_t G);

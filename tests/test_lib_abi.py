@@ -60,6 +60,38 @@ def test_store_argument_checks_before_launch():
     assert lib.pkv_store(base + 2, 128, base, 128, base, base, base, 1, 4, 16, 2, 64, None) == 1
 
 
+
+def test_store_decode_argument_checks_before_launch():
+    """pkv_store_decode rejects what pkv_decode rejects, plus bad new-token rows,
+    before any launch (so this runs without a GPU)."""
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(4096 + 16)
+    p = (ctypes.addressof(buf) + 15) // 16 * 16
+    row = 2 * 64  # H_kv * d
+
+    def sd(key=None, kst=row, value=None, vst=row, B=2, H_q=4, H_kv=2, d=64, bs=16, ws=1 << 20,
+           scale=0.125, wsp=None):
+        key = p if key is None else key
+        value = p if value is None else value
+        return lib.pkv_store_decode(p, p, key, kst, value, vst, p, p, p, p, B, H_q, H_kv, d, 8, bs,
+                                    3, scale, p if wsp is None else wsp, ws, None)
+
+    assert lib.pkv_store_decode(p, p, None, row, p, row, p, p, p, p, 2, 4, 2, 64, 8, 16, 3,
+                                0.125, p, 1 << 20, None) == 1   # null key
+    assert lib.pkv_store_decode(p, p, p, row, None, row, p, p, p, p, 2, 4, 2, 64, 8, 16, 3,
+                                0.125, p, 1 << 20, None) == 1   # null value
+    assert sd(kst=row - 8) == 1           # key stride below H_kv * d
+    assert sd(vst=row + 4) == 1           # value stride not a multiple of 8
+    assert sd(key=p + 2) == 1             # misaligned key
+    assert sd(value=p + 8) == 1           # misaligned value
+    assert sd(B=0) == 1
+    assert sd(H_q=6, H_kv=4) == 1         # H_q % H_kv != 0
+    assert sd(bs=24) == 1                 # not a power of two
+    assert sd(d=96) == 2                  # unsupported head size
+    assert sd(scale=float("nan")) == 1
+    ws = lib.pkv_decode_workspace_size(2, 4, 2, 64, 16, 3)
+    assert ws > 0 and sd(ws=ws - 1) == 1  # the decode's workspace size applies
+
 def test_attention_argument_checks_before_launch():
     lib = _lib.load()
     buf = ctypes.create_string_buffer(4096 + 16)
