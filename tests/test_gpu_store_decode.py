@@ -80,3 +80,35 @@ def test_store_decode_against_oracle():
     assert_bits_equal(fused.k_cache(), host.k_cache(), "k_cache vs oracle store")
     assert_bits_equal(fused.v_cache(), host.v_cache(), "v_cache vs oracle store")
     assert_close(out, ref, "store_decode vs oracle")
+
+
+def test_store_decode_clamped_length_stores_nothing():
+    """A context length beyond the table's capacity is clamped (as pkv_decode
+    clamps it): the new token has no slot, so nothing is stored, and the output
+    is pkv_decode's over the clamped length."""
+    bs, H_q, H_kv, d = 16, 4, 2, 64
+    lens = [20, 33, 48]
+    plan = custom_plan([(n - 1, 1) for n in lens], bs, H_q, H_kv, d, seed=5, extra_blocks=2,
+                       max_blocks_per_seq=3)
+    tens = make_tensors(plan, DEV, poison=False)
+    meta = pkv.prepare_metadata(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    dm = device_meta(meta, DEV)
+    cl = dm["context_lens"].clone()
+    cl[1] = 3 * bs + 5  # beyond 3 blocks of 16
+    sc = scale_of(d)
+    before_k, before_v = tens.k_cache().clone(), tens.v_cache().clone()
+    ref = pkv.decode(tens.q[0], tens.k_cache(), tens.v_cache(), dm["block_tables"], cl, sc)
+    out = pkv.store_decode(tens.q[0], tens.k_new(), tens.v_new(), tens.k_cache(), tens.v_cache(),
+                           dm["block_tables"], cl, sc)
+    torch.cuda.synchronize()
+    # rows of sequences 0 and 2 stored, nothing else changed
+    slots = meta["slot_mapping"].tolist()
+    exp_k, exp_v = before_k.clone(), before_v.clone()
+    for b in (0, 2):
+        blk, off = divmod(slots[b], bs)
+        exp_k[blk, off] = tens.k_new()[b]
+        exp_v[blk, off] = tens.v_new()[b]
+    assert_bits_equal(tens.k_cache(), exp_k.cpu(), "k_cache with a clamped length")
+    assert_bits_equal(tens.v_cache(), exp_v.cpu(), "v_cache with a clamped length")
+    # sequence 1 attends over its (clamped) cached rows exactly as pkv_decode does
+    assert_bits_equal(out[1], ref[1].cpu(), "output of the clamped sequence")
