@@ -203,8 +203,7 @@ pkv_status pkv_store_decode(void* out, const void* q, const void* key, int64_t k
   if (!workspace || workspace_bytes < plan.workspace_bytes || !aligned16(workspace))
     return PKV_EINVAL;
   const pkv::NewToken nt{static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
-                         key_stride, value_stride, static_cast<uint16_t*>(k_cache),
-                         static_cast<uint16_t*>(v_cache)};
+                         key_stride, value_stride};
   return launch_status(pkv::launch_decode(
       static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache), block_tables,

@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   struct Meta {
     int b, h, flags, k;
     int rows;  // valid key rows of the tile (0 for an empty tile)
-    int64_t new_row;  // kNewRow: element offset of the new token's rows in the caches
+    int new_row;  // kNewRow: the new token's row (slot) in the caches
   };
 
   // q of the next pieces is loaded by the load cursor when it reaches their
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     }
     if (from_new && real && blk_ok) {
       mt.flags |= kNewRow;
-      mt.new_row = (row0 + last) * rs + (int64_t)L.h * D;
+      mt.new_row = (int)(row0 + last);  // a slot: below num_blocks * block_size <= INT32_MAX
     }
     const uint16_t* kn = from_new ? nt_in.key + (int64_t)L.b * nt_in.key_stride + (int64_t)L.h * D : kt;
     const uint16_t* vn = from_new ? nt_in.value + (int64_t)L.b * nt_in.value_stride + (int64_t)L.h * D : vt;
@@ -744,14 +744,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 
   // The fused store: the lanes holding the tile's last row (the new token,
   // read from the new K/V input) write it into the caches.
+  // (The caches are written through the kernel's own cache pointers: the
+  // call's caches are not const, and this row is read by no one in the call.)
   auto store_new_row = [&](const u32x4 (&kx)[TPL][NW], const u32x4 (&vx)[TPL][NW], const Meta& mt) {
+    const int64_t at = (int64_t)mt.new_row * rs + (int64_t)mt.h * D;
+    uint16_t* kd = const_cast<uint16_t*>(k_cache) + at;
+    uint16_t* vd = const_cast<uint16_t*>(v_cache) + at;
 #pragma unroll
     for (int i = 0; i < TPL; ++i) {
       if (grp + i * TPI != mt.rows - 1) continue;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        st16(nt_in.k_cache + mt.new_row + dofs(w), kx[i][w]);
-        st16(nt_in.v_cache + mt.new_row + dofs(w), vx[i][w]);
+        st16(kd + dofs(w), kx[i][w]);
+        st16(vd + dofs(w), vx[i][w]);
       }
     }
   };

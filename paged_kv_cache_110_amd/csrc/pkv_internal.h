@@ -59,8 +59,6 @@ struct NewToken {
   const uint16_t* value;
   int64_t key_stride;
   int64_t value_stride;
-  uint16_t* k_cache;  // the caches again, as the store's destination
-  uint16_t* v_cache;
 };
 
 // Decode launch plan: one wavefront per resident slot of the current device.
