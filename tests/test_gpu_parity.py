@@ -107,6 +107,42 @@ def test_prefill_long_sequence():
     _full_check(plan)
 
 
+
+@pytest.mark.parametrize("geom", [(256, 16, 8, 128), (64, 32, 4, 64)],
+                         ids=lambda g: "bs%d_Hq%d_Hkv%d_d%d" % g)
+def test_prefill_long_context(geom):
+    """A long prompt behind a long cached prefix (8192 + 8192 keys: 128 query tiles, 256 key
+    tiles for the last ones), beside a short one; sampled rows, each the oracle's decode of
+    that row (prefill of one row equals decode, pinned on the CPU)."""
+    bs, H_q, H_kv, d = geom
+    log(f"long-context prefill {geom}")
+    plan = custom_plan([(8192, 8192), (0, 300)], bs, H_q, H_kv, d, seed=29, extra_blocks=2,
+                       kind="prefill")
+    tens = make_tensors(plan, DEV, poison=True)
+    host = cpu_copy(tens)
+    meta = pkv.prepare_metadata(plan.seqs, plan.block_size, plan.max_blocks_per_seq)
+    dm = device_meta(meta, DEV)
+    gpu_store(plan, tens, dm)
+    out = gpu_attention(plan, tens, dm)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    ometa = oracle_meta(plan)
+    oracle_store(host, ometa)
+    rows, tables, ctx = [], [], []
+    g = torch.Generator().manual_seed(31)
+    for b, s in enumerate(plan.seqs):
+        start = ometa["cu_seqlens_q"][b]
+        edges = {0, 1, 63, 64, 65, s.num_new - 1}
+        pick = {i for i in edges if i < s.num_new}
+        pick |= set(torch.randint(0, s.num_new, (24,), generator=g).tolist())
+        for i in sorted(pick):
+            rows.append(start + i)
+            tables.append(ometa["block_tables"][b])
+            ctx.append(s.num_cached + i + 1)
+    ref = O.default().decode(host.q[0][rows], host.k_cache(), host.v_cache(), tables, ctx,
+                             scale_of(d))
+    assert_close(out[rows], ref, f"long-context prefill {geom}, {len(rows)} sampled rows")
+
 def test_prefill_shared_prefix():
     log("prefill with shared prefix blocks")
     bs = 16
