@@ -223,6 +223,15 @@ def test_full_size_decode(name):
     assert_close(out, ref, f"{name} all {plan.B} sequences")
 
 
+def test_decode_one_very_long_sequence():
+    """A 131072-token sequence beside a 37-token one: each KV head of the long
+    sequence is cut into many pieces over the device's wavefronts, which the
+    merge combines.  Every output, against the oracle."""
+    log("decode of a 131072-token sequence beside a 37-token one")
+    plan = custom_plan([(131071, 1), (36, 1)], 256, 16, 8, 128, seed=41, extra_blocks=2)
+    _full_check(plan)
+
+
 def test_full_size_prefix_prefill():
     log("full-size prefix_prefill")
     plan = make_plan("prefix_prefill")
