@@ -46,7 +46,13 @@
 //  - a segment that lies inside one share is finished in place and written as
 //    bf16.  A segment cut by share boundaries writes an fp32 partial
 //    (m, l, acc[d]) per piece into its share's partial slots, and
-//    decode_merge_kernel combines the pieces in share order.
+//    decode_merge_kernel combines the pieces in share order;
+//  - with the step's store fused in (FUSE, pkv_store_decode), the wavefront
+//    that loads a segment's last tile takes the new token's row (and the
+//    masked rows after it) from the new K/V input rather than the cache, and
+//    writes that row into the cache before computing the tile.  No other tile
+//    holds the row, so nothing else reads it, and the kernel never reads a
+//    cache row it writes.
 #include <limits.h>
 #include <stdlib.h>
 
