@@ -165,7 +165,6 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
-
 def store_decode(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
                  v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                  softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
