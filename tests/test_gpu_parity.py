@@ -107,7 +107,6 @@ def test_prefill_long_sequence():
     _full_check(plan)
 
 
-
 @pytest.mark.parametrize("geom", [(256, 16, 8, 128), (64, 32, 4, 64)],
                          ids=lambda g: "bs%d_Hq%d_Hkv%d_d%d" % g)
 def test_prefill_long_context(geom):

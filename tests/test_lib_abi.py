@@ -60,7 +60,6 @@ def test_store_argument_checks_before_launch():
     assert lib.pkv_store(base + 2, 128, base, 128, base, base, base, 1, 4, 16, 2, 64, None) == 1
 
 
-
 def test_store_decode_argument_checks_before_launch():
     """pkv_store_decode rejects what pkv_decode rejects, plus bad new-token rows,
     before any launch (so this runs without a GPU)."""
