@@ -95,3 +95,16 @@ def test_decode_workspace_reuse_is_deterministic():
     for i in (1, 2):
         assert torch.equal(outs[0].view(torch.int16), outs[i].view(torch.int16)), f"call {i}"
     assert_close(outs[0], ref, "decode with a reused workspace")
+
+
+@pytest.mark.parametrize("H_q", [16, 32], ids=["G2_valu", "G4_mfma"])
+def test_decode_many_short_sequences(H_q):
+    # four times as many sequences as resident wavefronts, most shorter than
+    # one 16-token tile, with zero-length padding rows spread over the batch
+    # (inside and beyond the sequences whose offsets sit in LDS)
+    g = torch.Generator().manual_seed(21 + H_q)
+    lens = [int(x) for x in torch.randint(1, 65, (8192,), generator=g)]
+    log(f"decode with {len(lens)} short sequences, H_q {H_q}")
+    plan = _plan(lens, 16, H_q, 8, 128, seed=21 + H_q)
+    outs, ref = _run(plan, pad_rows=(0, 511, 512, 4095, 8191))
+    assert_close(outs[0], ref, f"decode B=8192 H_q={H_q}")
