@@ -98,6 +98,20 @@ def test_prefill_random_shapes(geom):
     _full_check(plan)
 
 
+
+@pytest.mark.parametrize("geom", [(16, 16, 8, 128), (32, 64, 8, 64)],
+                         ids=lambda g: "bs%d_Hq%d_Hkv%d_d%d" % g)
+def test_prefill_many_tiny_sequences(geom):
+    # thousands of sequences of 0-4 new tokens behind 0-300 cached ones: one
+    # partly filled query tile each (or none), most keys behind a cached prefix
+    bs, H_q, H_kv, d = geom
+    g = torch.Generator().manual_seed(17 + bs)
+    specs = [(int(c), int(n)) for c, n in zip(torch.randint(0, 301, (3000,), generator=g),
+                                              torch.randint(0, 5, (3000,), generator=g))]
+    log(f"prefill of {len(specs)} tiny sequences, geom {geom}")
+    plan = custom_plan(specs, bs, H_q, H_kv, d, seed=17 + bs, extra_blocks=3, kind="prefill")
+    _full_check(plan)
+
 def test_prefill_long_sequence():
     # more new tokens than the benchmark's sequences (several query tiles past 2048),
     # behind a cached prefix that ends mid-block
