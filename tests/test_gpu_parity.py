@@ -112,6 +112,24 @@ def test_prefill_many_tiny_sequences(geom):
     plan = custom_plan(specs, bs, H_q, H_kv, d, seed=17 + bs, extra_blocks=3, kind="prefill")
     _full_check(plan)
 
+
+HEAD_COUNT_GEOMS = [  # (block_size, H_q, H_kv, d): multi-head (G = 1) with many heads, odd KV head counts
+    (16, 32, 32, 128), (64, 12, 3, 64), (32, 40, 5, 128), (256, 6, 3, 128),
+]
+
+
+@pytest.mark.parametrize("geom", HEAD_COUNT_GEOMS, ids=lambda g: "bs%d_Hq%d_Hkv%d_d%d" % g)
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_unusual_head_counts(geom, kind):
+    bs, H_q, H_kv, d = geom
+    log(f"{kind} with H_q {H_q}, H_kv {H_kv}, d {d}, block size {bs}")
+    if kind == "decode":
+        specs = [(n - 1, 1) for n in (1, 17, 300, 2500, 64, 999)]
+    else:
+        specs = [(0, 1), (0, 77), (bs + 3, 200), (5, 0), (700, 130)]
+    plan = custom_plan(specs, bs, H_q, H_kv, d, seed=31 + H_kv, extra_blocks=2, kind=kind)
+    _full_check(plan)
+
 def test_prefill_long_sequence():
     # more new tokens than the benchmark's sequences (several query tiles past 2048),
     # behind a cached prefix that ends mid-block
